@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark one full absorbed-MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  mla_absorb_q (q_nope . W_UK, concat q_rope)  ->  mla_decode (split plan,
+  split-KV attention against the latent cache, log-sum-exp combine)  ->
+  mla_absorb_o (out . W_UV).
+Default workload: DeepSeek-V2/V3-shaped decode, bf16, batch 64, 128 heads,
+4096 cached tokens per sequence (latent cache [64, 4096, 576]).  That
+configuration gives no projection weights; the absorb inputs (q_nope, q_rope,
+W_UK, W_UV) are synthesized with the recipe of the end-to-end configuration.
+
+Timing: W untimed warm-up steps, then exactly K timed steps.  Before each
+timed step a 512 MiB buffer is overwritten (outside the timed events) so the
+latent cache cannot be served from the 4 MB L2s or the 256 MB Infinity Cache.
+HIP events on the library's stream bracket every step and, through the
+library's profiling hook, the split-KV attention kernel alone.  The whole
+timed loop is bracketed by torch.cuda.synchronize() on both sides.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOP/s + HBM GB/s (% of roofline), b=64 h=128 T=4096 bf16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+D_C, D_R, D_QK, D_K, D_V = 512, 64, 576, 128, 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", "decode_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work_counts(b, h, lens, elt=2):
+    """Algorithmic FLOPs and bytes of each step stage."""
+    sum_l = int(sum(lens))
+    dec_flop = 2 * (D_QK + D_C) * h * sum_l
+    dec_bytes = sum_l * D_QK * elt + b * h * (D_QK * elt + D_C * elt + 4)
+    aq_flop = 2 * b * h * D_K * D_C
+    aq_bytes = b * h * (D_K + D_R + D_QK) * elt + h * D_K * D_C * elt
+    ao_flop = 2 * b * h * D_C * D_V
+    ao_bytes = b * h * (D_C + D_V) * elt + h * D_C * D_V * elt
+    return {"decode": (dec_flop, dec_bytes), "absorb_q": (aq_flop, aq_bytes),
+            "absorb_o": (ao_flop, ao_bytes)}
+
+
+class Hip:
+    """Just enough of the HIP runtime (events) through ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per split-kernel launch from committed rocprofv3 --pmc runs,
+    valid only while the kernel source is unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole batch rows, all heads, absorb -> latent decode -> absorb."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    lens = w.seqlens.cpu().tolist()
+    wk = w_uk.cpu()
+    wv = w_uv.cpu()
+
+    def run(rows):
+        L = max(int(lens[r]) for r in rows)
+        qn, qr = q_nope[rows].cpu(), q_rope[rows].cpu()
+        c = w.cache[rows, :L].cpu()
+        sl = np.array([lens[r] for r in rows], np.int32)
+        cf = oracle._f64(c)  # widen outside the timed region
+        t0 = time.perf_counter()
+        qp = orc.absorb_q(qn, wk, qr)
+        out, _ = orc.decode_latent(qp, cf, sl, w.scale)
+        orc.absorb_o(out, wv)
+        dt = time.perf_counter() - t0
+        cnt = work_counts(len(rows), w.h, [lens[r] for r in rows])
+        return dt, sum(f for f, _ in cnt.values())
+
+    dt1, f1 = run([0])
+    n = int(min(w.b if max_rows is None else max_rows, max(1, round(target_s / max(dt1, 1e-3)))))
+    rows = list(range(n))
+    dt, fl = run(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d batch rows, all %d heads, %d cached tokens each: fp64 absorb_q -> "
+                      "latent-form decode -> absorb_o, %.1f s" % (n, w.b, w.h, lens[0], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload configuration (1..5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--n-chunks", type=int, default=0)
+    ap.add_argument("--hpg", type=int, default=0, help="heads per workgroup (0 = auto)")
+    ap.add_argument("--variant", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_decode_amd as mla
+    import workloads
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[args.config]
+    t_setup = time.perf_counter()
+    w = workloads.make(args.config, device="cuda", poison=False)
+    if cfg.raw_query:
+        q_nope, q_rope, w_uk, w_uv = w.q_nope, w.q_rope, w.w_uk, w.w_uv
+    else:
+        q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(w.b, w.h, dtype=w.dtype,
+                                                                 device="cuda")
+    lens = w.seqlens.cpu().tolist()
+    sched = {}
+    if args.n_chunks:
+        sched["n_chunks"] = args.n_chunks
+    if args.hpg:
+        sched["heads_per_group"] = args.hpg
+    if args.variant:
+        sched["variant"] = args.variant
+    bufs = mla.alloc_step(w.b, w.h, w.t_max, w.dtype, config=sched or None)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log("setup %.1f s: %s b=%d h=%d t_max=%d sum(L)=%d dtype=%s" %
+        (time.perf_counter() - t_setup, cfg.name, w.b, w.h, w.t_max, sum(lens), w.dtype))
+
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    ev = [[hip.event() for _ in range(4)] for _ in range(K)]
+
+    def step(i=None):
+        c = dict(sched)
+        if i is not None:
+            c["profile_events"] = (ev[i][1].value, ev[i][2].value)
+        mla.mla_step(q_nope, q_rope, w_uk, w_uv, w.cache, w.seqlens, w.scale, bufs,
+                     config=c or None)
+
+    for _ in range(W):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        hip.record(ev[i][0], stream)
+        step(i)
+        hip.record(ev[i][3], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [hip.elapsed_ms(e[0], e[3]) for e in ev]
+    kern_ms = [hip.elapsed_ms(e[1], e[2]) for e in ev]
+
+    # back-to-back steps (no eviction): context only
+    torch.cuda.synchronize()
+    b0, b1 = hip.event(), hip.event()
+    hip.record(b0, stream)
+    for _ in range(K):
+        step()
+    hip.record(b1, stream)
+    torch.cuda.synchronize()
+    b2b_ms = hip.elapsed_ms(b0, b1) / K
+
+    cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize)
+    step_flop = sum(f for f, _ in cnt.values())
+    step_bytes = sum(bb for _, bb in cnt.values())
+    dec_flop, dec_bytes = cnt["decode"]
+    ms = sum(step_ms) / K
+    kms = sum(kern_ms) / K
+    value = step_flop / (ms * 1e-3) / 1e12
+    k_gbs = dec_bytes / (kms * 1e-3) / 1e9
+    k_tfl = dec_flop / (kms * 1e-3) / 1e12
+    traffic = load_traffic(cfg.name)
+    log("step: mean %.2f us (min %.2f, max %.2f); split-KV kernel mean %.2f us (min %.2f); "
+        "back-to-back step %.2f us; wall %.3f s for %d steps" %
+        (ms * 1e3, min(step_ms) * 1e3, max(step_ms) * 1e3, kms * 1e3, min(kern_ms) * 1e3,
+         b2b_ms * 1e3, wall, K))
+    log("split-KV kernel: %.1f GB/s (%.1f%% of HBM), %.1f TFLOP/s (%.1f%% of bf16 MFMA)" %
+        (k_gbs, 100 * k_gbs / HBM_PEAK_GBS, k_tfl, 100 * k_tfl / MFMA_BF16_PEAK_TFLOPS))
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": w.b, "heads": w.h, "cached_tokens": w.t_max,
+                   "sum_cached_tokens": int(sum(lens)), "d_latent": D_C, "d_rope": D_R,
+                   "step": "absorb_q + decode (plan, split-KV, combine) + absorb_o",
+                   "cache_evicted_between_steps": flush is not None,
+                   "schedule": sched or "auto"},
+        "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_flop": step_flop,
+        "step_bytes": step_bytes,
+        "ms_per_step_back_to_back": round(b2b_ms, 5),
+        "roofline": {"kernel": "split-KV attention (decode_bf16_kernel)",
+                     "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "launch_us": round(kms * 1e3, 2),
+                     "alg_bytes_per_launch": dec_bytes},
+        "mfma": {"achieved": round(k_tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(k_tfl / MFMA_BF16_PEAK_TFLOPS, 4), "alg_flop_per_launch": dec_flop},
+    }
+    if not args.no_cpu_baseline:
+        t_c = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline(w, q_nope, q_rope, w_uk, w_uv)
+        log("cpu baseline %.1f s" % (time.perf_counter() - t_c))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""libmla355: absorbed Multi-head Latent Attention (MLA) decode on one AMD MI355X.
+
+Thin ctypes binding over the C ABI in ``include/mla355.h``.  Every function
+takes torch tensors (device memory and streams are torch's), checks dtype,
+device, shape and contiguity, and passes raw pointers plus the current HIP
+stream to the library.  No arithmetic happens here: every step of the path
+runs in the library's HIP kernels.
+
+The shared object ``libmla355.so`` is built in-tree by ``build.py``; importing
+this package without it raises immediately (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla355.so")
+
+D_C, D_R, D_QK, D_K, D_V = 512, 64, 576, 128, 128
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+MLA_DTYPE_F32 = 0
+MLA_DTYPE_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libmla355.so is not built (expected at %s); run "
+        "`python -m head_latent_attention_decode_amd.build` first" % LIB_PATH)
+
+
+class MLAConfig(ctypes.Structure):
+    """Mirror of mla_decode_config_t (scheduling overrides; zero = automatic)."""
+    _fields_ = [("n_chunks", ctypes.c_int), ("heads_per_group", ctypes.c_int),
+                ("variant", ctypes.c_int), ("reserved", ctypes.c_int * 5),
+                ("profile_events", ctypes.c_void_p * 2)]
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _ci, _cf, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.mla_abi_version.restype = _ci
+_lib.mla_status_string.restype = ctypes.c_char_p
+_lib.mla_status_string.argtypes = [_ci]
+_lib.mla_absorb_q.restype = _ci
+_lib.mla_absorb_q.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp, _vp]
+_lib.mla_absorb_o.restype = _ci
+_lib.mla_absorb_o.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp]
+_lib.mla_decode_workspace_bytes.restype = _sz
+_lib.mla_decode_workspace_bytes.argtypes = [_ci, _ci, _ci, _ci]
+_lib.mla_decode_workspace_bytes_ex.restype = _sz
+_lib.mla_decode_workspace_bytes_ex.argtypes = [_ci, _ci, _ci, _ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode.restype = _ci
+_lib.mla_decode.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
+_lib.mla_decode_ex.restype = _ci
+_lib.mla_decode_ex.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
+                               ctypes.POINTER(MLAConfig), _vp]
+
+EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
+                    "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
+                    "mla_decode_ex")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" %
+                         (where, _lib.mla_status_string(status).decode(), status))
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    if dt == torch.float32:
+        return MLA_DTYPE_F32
+    raise TypeError("libmla355 supports bfloat16 and float32, got %s" % dt)
+
+
+def _dev(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def abi_version() -> int:
+    return _lib.mla_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.mla_status_string(status).decode()
+
+
+def _cfg(config):
+    if config is None:
+        return None
+    if isinstance(config, MLAConfig):
+        return ctypes.pointer(config)
+    c = MLAConfig()
+    for k, v in dict(config).items():
+        if k == "profile_events":
+            c.profile_events[0] = v[0]
+            c.profile_events[1] = v[1]
+        else:
+            setattr(c, k, int(v))
+    return ctypes.pointer(c)
+
+
+def mla_decode_workspace_bytes(dtype: torch.dtype, b: int, h: int, t_max: int, config=None) -> int:
+    """Bytes of workspace mla_decode needs (pure host computation, no GPU)."""
+    if config is None:
+        return int(_lib.mla_decode_workspace_bytes(_dtype_code(dtype), b, h, t_max))
+    return int(_lib.mla_decode_workspace_bytes_ex(_dtype_code(dtype), b, h, t_max, _cfg(config)))
+
+
+def mla_absorb_q(q_nope, w_uk, q_rope, q_prime=None, stream=None):
+    """q'[b,h,:512] = q_nope[b,h,:] @ W_UK[h];  q'[b,h,512:] = q_rope[b,h,:]."""
+    b, h, _ = q_nope.shape
+    dt = q_nope.dtype
+    if q_prime is None:
+        q_prime = torch.empty((b, h, D_QK), dtype=dt, device=q_nope.device)
+    args = (_dev(q_nope, "q_nope", (b, h, D_K), dt), _dev(w_uk, "w_uk", (h, D_K, D_C), dt),
+            _dev(q_rope, "q_rope", (b, h, D_R), dt), _dev(q_prime, "q_prime", (b, h, D_QK), dt))
+    _check(_lib.mla_absorb_q(_dtype_code(dt), b, h, *args, _stream(stream)), "mla_absorb_q")
+    return q_prime
+
+
+def mla_absorb_o(o, w_uv, y=None, stream=None):
+    """y[b,h,:] = o[b,h,:] @ W_UV[h]."""
+    b, h, _ = o.shape
+    dt = o.dtype
+    if y is None:
+        y = torch.empty((b, h, D_V), dtype=dt, device=o.device)
+    args = (_dev(o, "o", (b, h, D_C), dt), _dev(w_uv, "w_uv", (h, D_C, D_V), dt),
+            _dev(y, "y", (b, h, D_V), dt))
+    _check(_lib.mla_absorb_o(_dtype_code(dt), b, h, *args, _stream(stream)), "mla_absorb_o")
+    return y
+
+
+def mla_decode(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, workspace=None,
+               config=None, stream=None):
+    """Latent-form MLA decode.  Returns (out [b,h,512], lse [b,h] fp32).
+
+    q_prime [b,h,576], cache [b,t_max,576] (same dtype), seqlens [b] int32 on the GPU.
+    workspace: optional uint8 GPU tensor of at least mla_decode_workspace_bytes bytes.
+    config: optional scheduling overrides (dict or MLAConfig).
+    """
+    b, h, _ = q_prime.shape
+    t_max = cache.shape[1]
+    dt = q_prime.dtype
+    dev = q_prime.device
+    _dev(q_prime, "q_prime", (b, h, D_QK), dt)
+    _dev(cache, "cache", (b, t_max, D_QK), dt)
+    if out is None:
+        out = torch.empty((b, h, D_C), dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((b, h), dtype=torch.float32, device=dev)
+    need = mla_decode_workspace_bytes(dt, b, h, t_max, config)
+    if need == 0:
+        raise ValueError("invalid decode problem or config: b=%d h=%d t_max=%d" % (b, h, t_max))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    args = (_dev(q_prime, "q_prime", (b, h, D_QK), dt), _dev(cache, "cache", (b, t_max, D_QK), dt),
+            _dev(seqlens, "seqlens", (b,), torch.int32), ctypes.c_float(float(softmax_scale)),
+            _dev(out, "out", (b, h, D_C), dt), _dev(lse, "lse", (b, h), torch.float32),
+            ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()))
+    if config is None:
+        st = _lib.mla_decode(_dtype_code(dt), b, h, t_max, *args, _stream(stream))
+    else:
+        st = _lib.mla_decode_ex(_dtype_code(dt), b, h, t_max, *args, _cfg(config), _stream(stream))
+    _check(st, "mla_decode")
+    return out, lse
+
+
+@dataclass
+class StepBuffers:
+    """Pre-allocated buffers for a full absorb -> decode -> absorb step."""
+    q_prime: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+    y: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_step(b, h, t_max, dtype=torch.bfloat16, device="cuda", config=None) -> StepBuffers:
+    need = mla_decode_workspace_bytes(dtype, b, h, t_max, config)
+    return StepBuffers(
+        q_prime=torch.empty((b, h, D_QK), dtype=dtype, device=device),
+        out=torch.empty((b, h, D_C), dtype=dtype, device=device),
+        lse=torch.empty((b, h), dtype=torch.float32, device=device),
+        y=torch.empty((b, h, D_V), dtype=dtype, device=device),
+        workspace=torch.empty(need, dtype=torch.uint8, device=device))
+
+
+def mla_step(q_nope, q_rope, w_uk, w_uv, cache, seqlens, softmax_scale, bufs: StepBuffers,
+             config=None, stream=None):
+    """mla_absorb_q -> mla_decode -> mla_absorb_o on one stream (no allocation)."""
+    mla_absorb_q(q_nope, w_uk, q_rope, bufs.q_prime, stream=stream)
+    mla_decode(bufs.q_prime, cache, seqlens, softmax_scale, bufs.out, bufs.lse, bufs.workspace,
+               config=config, stream=stream)
+    mla_absorb_o(bufs.out, w_uv, bufs.y, stream=stream)
+    return bufs.y
+
+
+def default_scale() -> float:
+    return 1.0 / math.sqrt(D_K + D_R)

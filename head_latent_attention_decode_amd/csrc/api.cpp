@@ -1,0 +1,191 @@
+// C ABI of libmla355 (declared in include/mla355.h): argument validation,
+// scheduling choice, workspace carving and launch sequencing.
+//
+// Validation is pure host code and runs before any HIP call, so every error
+// path can be exercised without a GPU.
+#include "../../include/mla355.h"
+#include "mla355_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+using namespace mla355;
+
+namespace {
+
+// Whole-chip compute-unit count the automatic schedule is sized for (MI355X:
+// 8 XCDs x 32 CUs).  It is a constant, not a device query, so that the
+// workspace size stays a pure host function of the problem size.
+constexpr int kCUs = 256;
+constexpr int kMaxChunks = 65536;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Schedule {
+    int hpg;        // heads per workgroup group
+    int variant;    // bf16 kernel variant (0 for fp32)
+    int n_hg;       // head groups
+    int n_chunks;   // token chunks per head group
+    int min_chunk;  // smallest chunk (tokens)
+};
+
+int round_down8(int x) { return x < 8 ? 8 : x / 8 * 8; }
+
+mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* cfg, Schedule* s)
+{
+    if (cfg) {
+        for (int i = 0; i < 5; ++i)
+            if (cfg->reserved[i] != 0) return MLA_ERR_UNSUPPORTED;
+        if (cfg->n_chunks < 0 || cfg->heads_per_group < 0 || cfg->variant < 0)
+            return MLA_ERR_UNSUPPORTED;
+        if ((cfg->profile_events[0] == nullptr) != (cfg->profile_events[1] == nullptr))
+            return MLA_ERR_UNSUPPORTED;
+    }
+    if (dt == MLA_DTYPE_F32) {
+        s->hpg = 16;
+        s->variant = 0;
+        if (cfg && cfg->heads_per_group != 0 && cfg->heads_per_group != 16) return MLA_ERR_UNSUPPORTED;
+        if (cfg && cfg->variant != 0) return MLA_ERR_UNSUPPORTED;
+        s->min_chunk = 16;
+    } else {
+        int hpg = h <= 16 ? 16 : h <= 32 ? 32 : 64;
+        if (cfg && cfg->heads_per_group != 0) hpg = cfg->heads_per_group;
+        const int variant = (cfg && cfg->variant != 0) ? cfg->variant : 1;
+        if (!bf16_variant_exists(hpg, variant)) return MLA_ERR_UNSUPPORTED;
+        s->hpg = hpg;
+        s->variant = variant;
+        s->min_chunk = bf16_tile_tokens(hpg, variant);
+    }
+    s->n_hg = (h + s->hpg - 1) / s->hpg;
+    if (cfg && cfg->n_chunks != 0) {
+        if (cfg->n_chunks % 8 != 0 || cfg->n_chunks > kMaxChunks) return MLA_ERR_UNSUPPORTED;
+        s->n_chunks = cfg->n_chunks;
+    } else {
+        s->n_chunks = round_down8(kCUs / s->n_hg);
+    }
+    return MLA_OK;
+}
+
+bool dims_ok(int b, int h, int t_max)
+{
+    if (b <= 0 || h <= 0 || t_max < 0) return false;
+    if ((int64_t)b * (int64_t)t_max >= ((int64_t)1 << 31)) return false;
+    if ((int64_t)b * (int64_t)h >= ((int64_t)1 << 31) / kDqk) return false;
+    return true;
+}
+
+bool dtype_ok(mla_dtype_t dt) { return dt == MLA_DTYPE_F32 || dt == MLA_DTYPE_BF16; }
+
+mla_status_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA355_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s)
+{
+    switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+size_t mla_decode_workspace_bytes_ex(mla_dtype_t dt, int b, int h, int t_max,
+                                     const mla_decode_config_t* cfg)
+{
+    if (!dtype_ok(dt) || !dims_ok(b, h, t_max)) return 0;
+    Schedule s;
+    if (choose_schedule(dt, h, cfg, &s) != MLA_OK) return 0;
+    return workspace_layout(b, h, s.n_chunks).total;
+}
+
+size_t mla_decode_workspace_bytes(mla_dtype_t dt, int b, int h, int t_max)
+{
+    return mla_decode_workspace_bytes_ex(dt, b, h, t_max, nullptr);
+}
+
+mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* q_prime,
+                           const void* cache, const int32_t* seqlens, float softmax_scale,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           const mla_decode_config_t* cfg, void* stream)
+{
+    if (!dtype_ok(dt) || !dims_ok(b, h, t_max)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!q_prime || !cache || !seqlens || !out || !lse || !workspace) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_prime) || !aligned16(cache) || !aligned16(seqlens) || !aligned16(out) ||
+        !aligned16(lse) || ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    Schedule s;
+    const mla_status_t st = choose_schedule(dt, h, cfg, &s);
+    if (st != MLA_OK) return st;
+    const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks);
+    if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    int32_t* plan = (int32_t*)ws;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = cache;
+    p.plan = plan;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (float*)(ws + w.po_off);
+    p.b = b;
+    p.h = h;
+    p.t_max = t_max;
+    p.n_chunks = s.n_chunks;
+    p.n_hg = s.n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
+    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
+    hipError_t e = launch_plan(seqlens, b, t_max, s.n_chunks, s.min_chunk, plan, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
+    if (dt == MLA_DTYPE_BF16)
+        e = launch_decode_bf16(p, s.hpg, s.variant, hs);
+    else
+        e = launch_decode_f32(p, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
+    e = launch_combine(dt == MLA_DTYPE_BF16, plan, b, h, p.plse, p.po, out, lse, hs);
+    return hip_status(e);
+}
+
+mla_status_t mla_decode(mla_dtype_t dt, int b, int h, int t_max, const void* q_prime,
+                        const void* cache, const int32_t* seqlens, float softmax_scale, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return mla_decode_ex(dt, b, h, t_max, q_prime, cache, seqlens, softmax_scale, out, lse,
+                         workspace, workspace_bytes, nullptr, stream);
+}
+
+mla_status_t mla_absorb_q(mla_dtype_t dt, int b, int h, const void* q_nope, const void* w_uk,
+                          const void* q_rope, void* q_prime, void* stream)
+{
+    if (!dtype_ok(dt) || !dims_ok(b, h, 0)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!q_nope || !w_uk || !q_rope || !q_prime) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_rope) || !aligned16(q_prime))
+        return MLA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_absorb_q(dt == MLA_DTYPE_BF16, b, h, q_nope, w_uk, q_rope, q_prime,
+                                      (hipStream_t)stream));
+}
+
+mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,
+                          void* stream)
+{
+    if (!dtype_ok(dt) || !dims_ok(b, h, 0)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!o || !w_uv || !y) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(o) || !aligned16(w_uv) || !aligned16(y)) return MLA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_absorb_o(dt == MLA_DTYPE_BF16, b, h, o, w_uv, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

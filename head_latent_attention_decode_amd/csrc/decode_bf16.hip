@@ -1,0 +1,566 @@
+// Split-KV absorbed-MLA decode kernel, bf16 in / fp32 accumulate, for gfx950.
+//
+// What it computes (glossary "Multi-head Latent Attention", section on why
+// decode absorbs the matrices): every absorbed query head q'_h (576 wide:
+// q^C_h (W^UK_h)^T followed by the rope query) scores directly against the
+// shared latent rows [c_KV ; k_R]; the softmax-weighted sum of the c_KV parts
+// is the 512-wide output.  Per-head keys and values are never formed.
+//
+// How (one workgroup = one token chunk x one group of HG = HS*WH heads):
+//  * Tiles of N = TS*NT latent rows stream HBM -> LDS with direct-to-LDS
+//    16-byte DMA loads (global_load_lds_dwordx4), STAGES deep, one copy per
+//    workgroup shared by all its heads.  A tile is stored as two regions:
+//      A: the first 1024 B of every row (c_KV), 1 KB per row, so one wave DMA
+//         instruction moves one row;
+//      B: the last 128 B of every row (k_R), 8 rows per DMA instruction.
+//    16-byte chunks are XOR-swizzled inside each row (chunk c of row r sits at
+//    c ^ xA(r) in region A, c ^ xB(r) in region B) so that the MFMA operand
+//    reads of consecutive rows fall in distinct LDS banks.
+//  * Each wave owns WH heads (16 -> v_mfma_f32_16x16x32_bf16, 32 ->
+//    v_mfma_f32_32x32x16_bf16) and NT tokens of each tile:
+//      S^T = K . Q'^T     A = latent rows from LDS (ds_read_b128),
+//                         B = the wave's queries, resident in VGPRs.
+//      O^T += V^T . P^T   A = latent rows read transposed from LDS
+//                         (ds_read_b64_tr_b16), B = P^T straight from the
+//                         S^T accumulator layout (no data movement).
+//    In both products every lane holds exactly one head, so the online
+//    softmax state (running max m, running sum l, rescale) is lane-local;
+//    the per-tile max needs one or two cross-lane steps.
+//  * Online softmax in base 2 (scale * log2 e folded into the scores).  The
+//    accumulator is only rescaled when the running max grows by more than
+//    2^8 (values stay far inside fp32 range); the final normalisation uses the
+//    same max for l and O, so this is exact.
+//  * TS > 1: the TS waves of one head subgroup split each tile's tokens and
+//    merge their (m, l, O) through LDS at the end of a segment.
+//  * Segment end: a row finished inside this chunk writes out (bf16) and lse;
+//    otherwise the normalised fp32 partial and its lse go to the row's slot.
+#include "mla355_internal.h"
+
+#include <math.h>
+
+namespace mla355 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef LDS_AS unsigned char lds_byte;
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest tolerated growth
+constexpr float kNegBig = -1.0e30f;        // finite "minus infinity" for the running max
+// Buffer resource word 3 for raw (untyped, unswizzled) buffer access on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).  Issued
+// through the builtin so that the compiler's own wait insertion sees it.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+// Workgroup barrier ordering LDS only: the fences make every LDS access
+// before the barrier complete (lgkmcnt) and keep the compiler from moving LDS
+// accesses across it, without waiting for outstanding global loads.  Tile
+// data arrives by DMA, so its completion is awaited separately (vmcnt) by
+// the issuing wave before the barrier.
+__device__ __forceinline__ void wg_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One LDS array per pipeline stage.  Distinct objects let the compiler prove
+// that reads of one stage do not alias DMA still landing in another, so it
+// does not insert conservative vmcnt(0) waits before them.
+template <int BYTES, int S>
+__device__ __forceinline__ lds_byte* stage_lds()
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[BYTES];
+    return (lds_byte*)buf;
+}
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int WH>
+struct Mfma;
+
+template <>
+struct Mfma<16> {
+    typedef f32x4_t acc_t;
+    static constexpr int kK = 32;      // contraction per instruction
+    static constexpr int kAcc = 4;     // fp32 accumulators per lane
+    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Region-A swizzle (4 bits): rows 0..15 all distinct (b128 reads of 16
+    // rows), and rows 0..7 / 8..15 land in distinct 32-byte pairs (b64
+    // transposed reads of a 16-column strip by 8 rows).
+    __device__ __forceinline__ static int xa(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+};
+
+template <>
+struct Mfma<32> {
+    typedef f32x16_t acc_t;
+    static constexpr int kK = 16;
+    static constexpr int kAcc = 16;
+    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // rows 0..15 distinct, and each run of 4 rows lands in distinct 64-byte
+    // quads (b64 transposed reads of a 32-column strip by 4 rows).
+    __device__ __forceinline__ static int xa(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+
+// Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.
+__device__ __forceinline__ int xb(int r) { return (r >> 1) & 7; }
+
+template <int WH, int HS, int TS, int NT, int STAGES>
+struct Tiling {
+    static constexpr int NW = HS * TS;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int HG = HS * WH;             // heads per workgroup
+    static constexpr int N = TS * NT;              // tokens per tile
+    static constexpr int A_BYTES = N * 1024;
+    static constexpr int TILE_BYTES = N * kRowBytesBf16;
+    static constexpr int LDS_BYTES = STAGES * TILE_BYTES;
+    static constexpr int LOADS_A = N / NW;         // region-A DMA instructions per wave
+    static constexpr int GROUPS_B = N / 8;         // region-B DMA instructions per tile
+    static constexpr int LOADS_B_MAX = (GROUPS_B + NW - 1) / NW;
+    static constexpr int LOADS = LOADS_A + LOADS_B_MAX;
+    static constexpr int KSTEPS = kDqk / Mfma<WH>::kK;
+    static constexpr int KSTEPS_A = kDc / Mfma<WH>::kK;   // steps inside region A
+    static constexpr int MBLK = kDc / WH;          // O^T blocks (WH latent columns each)
+    static constexpr int SBLK = NT / WH;           // S^T blocks per wave per tile
+    static constexpr int MERGE_FLOATS = MBLK * Mfma<WH>::kAcc + 2;  // per lane
+    static_assert(N % NW == 0, "region A rows split evenly over waves");
+    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+    static_assert(STAGES == 2 || GROUPS_B % NW == 0, "exact vmcnt accounting needs even B split");
+    static_assert(NT % 32 == 0 && NT % WH == 0, "wave token slice must be whole MFMA blocks");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((STAGES - 1) * LOADS <= 63, "vmcnt range");
+    static_assert(TS == 1 || (TS - 1) * HS * 64 * MERGE_FLOATS * 4 <= TILE_BYTES, "merge area");
+};
+
+template <int WH, int HS, int TS, int NT, int STAGES>
+__global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams p)
+{
+    using T = Tiling<WH, HS, TS, NT, STAGES>;
+    using M = Mfma<WH>;
+    typedef typename M::acc_t acc_t;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hs = wave % HS;
+    const int ts = wave / HS;
+    const int hl = lane & (WH - 1);   // this lane's head inside the wave's WH heads
+    const int grp = lane / WH;        // lane group sharing that head (0..64/WH-1)
+
+    // Workgroup -> (chunk k, head group hg).  Dispatch is round-robin over the
+    // 8 XCDs (block i -> XCD i % 8); all head groups of one chunk get the same
+    // XCD so they share its L2 copy of the chunk's tiles.
+    int k, hg;
+    if (p.n_hg == 1) {
+        k = blockIdx.x;
+        hg = 0;
+    } else {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        k = (slot / p.n_hg) * 8 + xcd;
+        hg = slot % p.n_hg;
+    }
+    const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
+    const int total = p.plan[0];
+    const int chunk = p.plan[1];
+    int r = pv.chunk_row()[k];
+    if (r < 0) return;
+    int pos = k * chunk;
+    const int end = pos + min(chunk, total - pos);  // no int overflow near 2^31 tokens
+
+    const __bf16* __restrict__ qg = (const __bf16*)p.q;
+    const unsigned char* __restrict__ cg = (const unsigned char*)p.cache;
+    const int head = hg * T::HG + hs * WH + hl;
+    const bool head_ok = head < p.h;
+    const int tok0 = ts * NT;  // this wave's first token in every tile
+
+    // ---- per-lane LDS byte offsets (relative to a stage base) --------------
+    // K reads (S^T A operand): lane -> token row tok0 + sb*WH + rr, logical
+    // chunk ks*(kK/8) + grp.  rr & 15 == lane & 15 for every sb.
+    const int rr = lane & (WH - 1);
+    constexpr int CPK = M::kK / 8;                    // chunks per k-step per lane group
+    constexpr int NQA = 16 / CPK;                     // distinct (c & 15) patterns in region A
+    constexpr int KSTEPS_B = T::KSTEPS - T::KSTEPS_A; // steps inside region B
+    int koffA[NQA], koffB[KSTEPS_B];
+    {
+        const int xa = M::xa(rr & 15);
+        const int xbv = xb(rr & 15);
+#pragma unroll
+        for (int q = 0; q < NQA; ++q) koffA[q] = (tok0 + rr) * 1024 + (((q * CPK + grp) ^ xa) << 4);
+#pragma unroll
+        for (int q = 0; q < KSTEPS_B; ++q)
+            koffB[q] = T::A_BYTES + (tok0 + rr) * 128 + (((q * CPK + grp) ^ xbv) << 4);
+    }
+    // V^T reads (transposed, region A).  See the ds_read_b64_tr_b16 mapping:
+    // inside each 16-lane group, source lane s supplies 4 consecutive columns
+    // of one row; output lane i, element e receives source lane 4e + i/4,
+    // element i%4.
+    constexpr int NQV = (WH == 16) ? 8 : 4;           // distinct column patterns
+    int voff0[NQV], voff1[NQV];
+    {
+        if (WH == 16) {
+            const int row0 = tok0 + grp * 4 + ((lane & 15) >> 2);  // + u*32, hi rows +16
+            const int x = M::xa(row0 & 15);
+            const int hb = (lane & 3) >> 1;
+#pragma unroll
+            for (int q = 0; q < NQV; ++q) {
+                voff0[q] = row0 * 1024 + (((2 * q + hb) ^ x) << 4) + ((lane & 1) << 3);
+                voff1[q] = 0;  // hi rows are row0 + 16: same swizzle, immediate offset
+            }
+        } else {
+            const int row0 = tok0 + (lane >> 5) * 4 + ((lane & 15) >> 2);  // + u*16, hi rows +8
+            const int x0 = M::xa(row0 & 15), x1 = M::xa((row0 + 8) & 15);
+            const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+            for (int q = 0; q < NQV; ++q) {
+                voff0[q] = row0 * 1024 + (((4 * q + cc) ^ x0) << 4) + ((lane & 1) << 3);
+                voff1[q] = (row0 + 8) * 1024 + (((4 * q + cc) ^ x1) << 4) + ((lane & 1) << 3);
+            }
+        }
+    }
+
+    while (true) {
+        const int row_lo = pv.cu()[r];
+        const int row_hi = pv.cu()[r + 1];
+        const int seg_end = min(end, row_hi);
+        const int seg_a = pos - row_lo;
+        const int seg_len = seg_end - pos;
+        const int split_j = k - row_lo / chunk;
+        const bool final_out = pv.nsplit()[r] == 1;
+        const int slot = pv.base()[r] + split_j;
+        const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
+        const int n_tiles = (seg_len + T::N - 1) / T::N;
+
+        // Queries: B operand of S^T = K . Q^T.  Lane -> head hl, k-slots
+        // grp*8 .. +7 of contraction step ks (k = ks*kK + grp*8 + j).
+        bf16x8_t qf[T::KSTEPS];
+        {
+            const bf16x8_t* qrow =
+                (const bf16x8_t*)(qg + ((size_t)r * p.h + (head_ok ? head : 0)) * kDqk);
+#pragma unroll
+            for (int ks = 0; ks < T::KSTEPS; ++ks) {
+                bf16x8_t v = qrow[ks * CPK + grp];
+                if (!head_ok) v = (bf16x8_t){};
+                qf[ks] = v;
+            }
+        }
+
+        auto issue_tile = [&](auto SC, int tile) {
+            const int t0 = tile * T::N;
+            const int last = min(T::N, seg_len - t0) - 1;  // last valid tile row
+            // Buffer resource over this tile's valid rows.  Rows past the end of
+            // the segment are clamped to the last valid row (finite data; their
+            // scores are masked), so no access leaves [t0, seg_len).
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(seg_base + (size_t)t0 * kRowBytesBf16), (short)0,
+                (last + 1) * kRowBytesBf16, kBufferFlags);
+            lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
+            // region A: one row per instruction; lane l fetches logical chunk l ^ xA(row).
+#pragma unroll
+            for (int j = 0; j < T::LOADS_A; ++j) {
+                const int row = wave + j * T::NW;
+                const int srow = min(row, last);   // rows past the end re-read a valid row
+                const unsigned voff = (unsigned)((lane ^ M::xa(row & 15)) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (LDS_AS void*)(st + row * 1024), 16, voff,
+                    __builtin_amdgcn_readfirstlane(srow * kRowBytesBf16), 0, 0);
+            }
+            // region B: 8 rows per instruction; lane l -> row 8*gb + l/8, slot l%8.
+#pragma unroll
+            for (int j = 0; j < T::LOADS_B_MAX; ++j) {
+                const int gb = wave + j * T::NW;
+                if (T::GROUPS_B % T::NW == 0 || gb < T::GROUPS_B) {
+                    const int row = gb * 8 + (lane >> 3);
+                    const int srow = min(row, last);
+                    const int lc = (lane & 7) ^ xb(row & 15);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rsrc, (LDS_AS void*)(st + T::A_BYTES + gb * 1024), 16,
+                        (unsigned)(srow * kRowBytesBf16 + 1024 + lc * 16), 0, 0, 0);
+                }
+            }
+        };
+
+        acc_t o[T::MBLK];
+#pragma unroll
+        for (int mb = 0; mb < T::MBLK; ++mb) o[mb] = (acc_t){};
+        float m_run = kNegBig;  // running max (base-2 scaled scores)
+        float l_run = 0.f;      // this lane's share of the running sum
+
+        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
+        if (STAGES > 2 && 1 < n_tiles) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
+        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
+
+        auto tile_body = [&](auto SC, int it) {
+            constexpr int S = decltype(SC)::value;
+            // Tiles issued after `it` so far: it+1 .. min(it+STAGES-2, n_tiles-1).
+            if (STAGES > 2 && n_tiles - 1 - it >= STAGES - 2)
+                wait_vmcnt<(STAGES > 2 ? (STAGES - 2) * T::LOADS : 0)>();
+            else
+                wait_vmcnt<0>();
+            wg_barrier();  // tile `it` visible to all waves; stage of tile it-1 free
+            if (it + STAGES - 1 < n_tiles) issue_tile(IC<(S + STAGES - 1) % STAGES>{}, it + STAGES - 1);
+
+            lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
+            const int tvalid = seg_len - it * T::N - tok0;  // valid tokens for this wave (may be <= 0)
+
+            // ---- S^T = K . Q^T -------------------------------------------------
+            acc_t sacc[T::SBLK];
+#pragma unroll
+            for (int sb = 0; sb < T::SBLK; ++sb) sacc[sb] = (acc_t){};
+#pragma unroll
+            for (int ks = 0; ks < T::KSTEPS; ++ks) {
+#pragma unroll
+                for (int sb = 0; sb < T::SBLK; ++sb) {
+                    const lds_byte* a;
+                    if (ks < T::KSTEPS_A)
+                        a = tb + koffA[ks % NQA] + (ks / NQA) * 256 + sb * WH * 1024;
+                    else
+                        a = tb + koffB[ks - T::KSTEPS_A] + sb * WH * 128;
+                    const bf16x8_t kf = *(const LDS_AS bf16x8_t*)a;
+                    sacc[sb] = M::mma(kf, qf[ks], sacc[sb]);
+                }
+            }
+
+            // ---- online softmax (lane-local head) ------------------------------
+            // sacc[sb][i] is the score of token tok0 + sb*WH + toff(i), head hl.
+            float tmax = -INFINITY;
+            const bool full = tvalid >= NT;
+#pragma unroll
+            for (int sb = 0; sb < T::SBLK; ++sb) {
+#pragma unroll
+                for (int i = 0; i < M::kAcc; ++i) {
+                    const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
+                    float v = sacc[sb][i] * p.scale_log2;
+                    if (!full && sb * WH + toff >= tvalid) v = -INFINITY;
+                    sacc[sb][i] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            }
+            if (WH == 16) tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float m_new = fmaxf(m_run, tmax);
+            if (__any(m_new > m_run + kRescaleThreshold)) {
+                const float alpha = exp2_fast(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb) o[mb] *= alpha;
+                m_run = m_new;
+            }
+            // P^T as the B operand of O^T += V^T . P^T.  WH = 16: slots 0..3 are
+            // block 2u's tokens grp*4+i, slots 4..7 block 2u+1's.  WH = 32: MFMA
+            // u = 2sb + v of block sb uses accumulator entries 8v .. 8v+7.
+            constexpr int NPB = NT / 32 * (WH == 16 ? 1 : 2);
+            bf16x8_t pb[NPB];
+#pragma unroll
+            for (int sb = 0; sb < T::SBLK; ++sb) {
+#pragma unroll
+                for (int i = 0; i < M::kAcc; ++i) {
+                    const float e = exp2_fast(sacc[sb][i] - m_run);
+                    l_run += e;
+                    if (WH == 16)
+                        pb[sb >> 1][(sb & 1) * 4 + i] = (__bf16)e;
+                    else
+                        pb[sb * 2 + (i >> 3)][i & 7] = (__bf16)e;
+                }
+            }
+
+            // ---- O^T += V^T . P^T ------------------------------------------------
+            // MFMA u covers 32 (WH=16) or 16 (WH=32) tokens starting at tok0 + u*TPU.
+            constexpr int TPU = (WH == 16) ? 32 : 16;
+#pragma unroll
+            for (int u = 0; u < NPB; ++u) {
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb) {
+                    const int q = mb % NQV;
+                    const int blk = (mb / NQV) * 256 + u * TPU * 1024;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4_t*)(tb + voff0[q] + blk));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4_t*)(tb + (WH == 16 ? voff0[q] + 16 * 1024 : voff1[q]) + blk));
+                    const bf16x4_t lo4 = __builtin_bit_cast(bf16x4_t, lo);
+                    const bf16x4_t hi4 = __builtin_bit_cast(bf16x4_t, hi);
+                    const bf16x8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[mb] = M::mma(a, pb[u], o[mb]);
+                }
+            }
+        };
+
+        for (int it0 = 0; it0 < n_tiles; it0 += STAGES) {
+            tile_body(IC<0>{}, it0);
+            if (STAGES > 1 && it0 + 1 < n_tiles) tile_body(IC<(STAGES > 1 ? 1 : 0)>{}, it0 + 1);
+            if (STAGES > 2 && it0 + 2 < n_tiles) tile_body(IC<(STAGES > 2 ? 2 : 0)>{}, it0 + 2);
+            if (STAGES > 3 && it0 + 3 < n_tiles) tile_body(IC<(STAGES > 3 ? 3 : 0)>{}, it0 + 3);
+        }
+
+        // ---- segment epilogue ------------------------------------------------
+        if (WH == 16) l_run += __shfl_xor(l_run, 16, 64);
+        l_run += __shfl_xor(l_run, 32, 64);
+
+        bool writer = true;
+        if (TS > 1) {
+            // Waves ts >= 1 publish (m, l, O); wave ts == 0 of the same head
+            // subgroup merges them.  The merge area overlays the tile stages,
+            // so first every wave must have finished reading the last tile.
+            wg_barrier();
+            float* area = (float*)stage_lds<T::TILE_BYTES, 0>();
+            if (ts > 0) {
+                float* dst = area + ((size_t)((ts - 1) * HS + hs) * T::MERGE_FLOATS) * 64;
+                dst[lane] = m_run;
+                dst[64 + lane] = l_run;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int i = 0; i < M::kAcc; ++i) dst[(2 + mb * M::kAcc + i) * 64 + lane] = o[mb][i];
+                writer = false;
+            }
+            wg_barrier();
+            if (ts == 0) {
+#pragma unroll
+                for (int t2 = 1; t2 < TS; ++t2) {
+                    const float* src = area + ((size_t)((t2 - 1) * HS + hs) * T::MERGE_FLOATS) * 64;
+                    const float m2 = src[lane];
+                    const float l2 = src[64 + lane];
+                    const float mm = fmaxf(m_run, m2);
+                    const float a1 = exp2_fast(m_run - mm);
+                    const float a2 = exp2_fast(m2 - mm);
+                    l_run = l_run * a1 + l2 * a2;
+#pragma unroll
+                    for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                        for (int i = 0; i < M::kAcc; ++i)
+                            o[mb][i] = o[mb][i] * a1 + src[(2 + mb * M::kAcc + i) * 64 + lane] * a2;
+                    m_run = mm;
+                }
+            }
+        }
+
+        if (writer && head_ok) {
+            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            // O^T accumulator entry i of block mb is latent column
+            //   WH=16: mb*16 + grp*4 + i       WH=32: mb*32 + (i/4)*8 + grp*4 + i%4
+            if (final_out) {
+                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < M::kAcc / 4; ++q4) {
+                        const int c = mb * WH + q4 * 8 + grp * 4;
+                        bf16x4_t v;
+                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                        *(bf16x4_t*)(orow + c) = v;
+                    }
+                if (grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
+            } else {
+                float* prow = p.po + ((size_t)slot * p.h + head) * kDc;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < M::kAcc / 4; ++q4) {
+                        const int c = mb * WH + q4 * 8 + grp * 4;
+                        f32x4_t v;
+                        v[0] = o[mb][q4 * 4 + 0] * inv;
+                        v[1] = o[mb][q4 * 4 + 1] * inv;
+                        v[2] = o[mb][q4 * 4 + 2] * inv;
+                        v[3] = o[mb][q4 * 4 + 3] * inv;
+                        *(f32x4_t*)(prow + c) = v;
+                    }
+                if (grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
+            }
+        }
+
+        pos = seg_end;
+        if (pos >= end) break;
+        // The next segment reuses the LDS stages: every wave must be done.
+        wg_barrier();
+        ++r;
+        while (pv.cu()[r + 1] <= pos) ++r;  // skip empty rows
+    }
+}
+
+template <int WH, int HS, int TS, int NT, int STAGES>
+hipError_t launch_variant(const DecodeParams& p, hipStream_t stream)
+{
+    using T = Tiling<WH, HS, TS, NT, STAGES>;
+    const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
+    decode_bf16_kernel<WH, HS, TS, NT, STAGES><<<grid, T::THREADS, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+struct VariantEntry {
+    int heads_per_group;
+    int variant;
+    int tile_tokens;
+    hipError_t (*launch)(const DecodeParams&, hipStream_t);
+};
+
+// heads_per_group, variant id, tile tokens, launcher <WH, HS, TS, NT, STAGES>
+const VariantEntry kVariants[] = {
+    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>},
+    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>},
+    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>},
+    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>},
+    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>},
+    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>},
+    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>},
+    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>},
+};
+
+const VariantEntry* find_variant(int hpg, int variant)
+{
+    if (variant == 0) variant = 1;
+    for (const auto& v : kVariants)
+        if (v.heads_per_group == hpg && v.variant == variant) return &v;
+    return nullptr;
+}
+
+}  // namespace
+
+bool bf16_variant_exists(int heads_per_group, int variant)
+{
+    return find_variant(heads_per_group, variant) != nullptr;
+}
+
+int bf16_tile_tokens(int heads_per_group, int variant)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    return v ? v->tile_tokens : 0;
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
+                              hipStream_t stream)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    if (!v) return hipErrorInvalidValue;
+    return v->launch(p, stream);
+}
+
+}  // namespace mla355

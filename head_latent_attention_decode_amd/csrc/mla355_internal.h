@@ -1,0 +1,105 @@
+// Internal declarations shared by the libmla355 host layer and its kernels.
+// Not installed; the public ABI is include/mla355.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla355 {
+
+constexpr int kDc = 512;       // latent width
+constexpr int kDr = 64;        // RoPE key width
+constexpr int kDqk = 576;      // latent row width
+constexpr int kDk = 128;       // per-head query width (absorb q)
+constexpr int kDv = 128;       // per-head value width (absorb o)
+constexpr int kRowBytesBf16 = kDqk * 2;  // 1152 B: 72 chunks of 16 B
+
+// ---------------------------------------------------------------------------
+// Split plan, built on the device from seqlens by plan_kernel.
+// The batch is viewed as one concatenated token sequence (row 0's tokens,
+// then row 1's, ...).  It is cut into n_chunks equal chunks of `chunk`
+// tokens; each chunk (per head group) is one workgroup's work.  A chunk may
+// cover the tail of one row and the head of the next; each (row, chunk)
+// intersection is a "segment" with its own softmax state.  A row cut into
+// several segments writes fp32 partials (normalised output + lse) into
+// numbered slots, merged afterwards by the log-sum-exp combine kernel; a row
+// that lies inside one chunk writes its final output directly.
+//
+// int32 layout (offsets in elements):
+//   [0] total tokens  [1] chunk  [2] n_chunks  [3] unused
+//   cu[b+1]        at 4              prefix sums of clamped lengths
+//   base[b]        at 4 + (b+1)      first partial slot of each row
+//   nsplit[b]      at 4 + (b+1) + b  segments per row (0 for an empty row)
+//   chunk_row[n]   at 4 + (b+1) + 2b first row touched by chunk k (-1: idle)
+// ---------------------------------------------------------------------------
+struct PlanView {
+    int32_t* p;
+    int b;
+    __host__ __device__ int32_t* cu() const { return p + 4; }
+    __host__ __device__ int32_t* base() const { return p + 4 + (b + 1); }
+    __host__ __device__ int32_t* nsplit() const { return p + 4 + (b + 1) + b; }
+    __host__ __device__ int32_t* chunk_row() const { return p + 4 + (b + 1) + 2 * b; }
+};
+
+struct WorkspaceLayout {
+    size_t plan_ints;   // int32 elements of the plan
+    size_t plse_off;    // byte offset of partial lse  [slots, h] fp32
+    size_t po_off;      // byte offset of partial out  [slots, h, 512] fp32
+    size_t total;       // bytes
+    int max_slots;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WorkspaceLayout workspace_layout(int b, int h, int n_chunks)
+{
+    WorkspaceLayout w;
+    w.plan_ints = 4 + (size_t)(b + 1) + 2 * (size_t)b + (size_t)n_chunks;
+    w.max_slots = n_chunks + b;  // every chunk adds at most one cut inside a row
+    w.plse_off = align_up(w.plan_ints * 4, 256);
+    w.po_off = align_up(w.plse_off + (size_t)w.max_slots * h * 4, 256);
+    w.total = align_up(w.po_off + (size_t)w.max_slots * h * kDc * 4, 256);
+    return w;
+}
+
+struct DecodeParams {
+    const void* q;        // [b,h,576] dtype
+    const void* cache;    // [b,t_max,576] dtype
+    const int32_t* plan;  // plan (see above)
+    void* out;            // [b,h,512] dtype
+    float* lse;           // [b,h]
+    float* plse;          // [slots,h]
+    float* po;            // [slots,h,512]
+    int b, h, t_max;
+    int n_chunks;         // chunks per head group
+    int n_hg;             // head groups
+    float scale_log2;     // softmax_scale * log2(e)
+};
+
+// Launchers (return hipGetLastError() after the launch).
+hipError_t launch_plan(const int32_t* seqlens, int b, int t_max, int n_chunks, int min_chunk,
+                       int32_t* plan, hipStream_t stream);
+hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
+                          const float* po, void* out, float* lse, hipStream_t stream);
+
+// bf16 decode variants.  heads_per_group selects the family; variant picks a
+// tiling inside it (0 = default).  Returns hipErrorInvalidValue if absent.
+struct Bf16Variant {
+    int heads_per_group;
+    int variant;
+    int tile_tokens;      // tokens per LDS tile (used for the minimum chunk)
+};
+bool bf16_variant_exists(int heads_per_group, int variant);
+int bf16_tile_tokens(int heads_per_group, int variant);
+hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
+                              hipStream_t stream);
+
+hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const void* w_uk,
+                           const void* q_rope, void* q_prime, hipStream_t stream);
+hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w_uv, void* y,
+                           hipStream_t stream);
+
+}  // namespace mla355

@@ -1,0 +1,160 @@
+/*
+ * mla355.h -- C ABI of libmla355: absorbed Multi-head Latent Attention (MLA)
+ * decode on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   Each cached token holds one latent row [c_KV (512) ; k_R (64)] shared by
+ *   every query head ("Multi-head Latent Attention", LLM glossary, layout
+ *   section; "MLA" notes, Dimensions: 512 + 64 = 576 per token).  Decode
+ *   never expands per-head keys or values.  Instead the key up-projection is
+ *   folded into the query (q absorb), attention scores run directly against
+ *   the latent rows, and the value up-projection is applied after the
+ *   softmax-weighted sum (o absorb) (glossary, section on why decode absorbs
+ *   the matrices).  FlashMLA issue 16 ("up matrix is not involved?") gives
+ *   the interface split: q absorb and o absorb are separate calls; attention
+ *   takes the 576-wide absorbed query and returns a 512-wide latent output.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to dense, row-major
+ *     (C-contiguous) arrays.  The caller owns every buffer.  The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL selects the default stream) and is asynchronous.
+ *   - Inputs are read only; outputs must not alias inputs.
+ *   - Every tensor base pointer must be 16-byte aligned (128-bit accesses);
+ *     the workspace must be 256-byte aligned.
+ *   - Errors: argument checks run on the host before anything is enqueued and
+ *     return a status; nothing is launched then.  A failed launch returns
+ *     MLA_ERR_HIP.  Nothing is printed, no exception or errno crosses the ABI.
+ *   - The library holds no mutable state: calls are thread-safe (two calls
+ *     that share output or workspace buffers must not overlap in time).
+ *   - dtype selects the element type of q_nope, q_rope, w_uk, w_uv, q_prime,
+ *     cache, out and y: MLA_DTYPE_BF16 (compute: bf16 MFMA, fp32
+ *     accumulation) or MLA_DTYPE_F32 (compute: fp32 throughout).  lse is
+ *     always fp32.
+ */
+#ifndef MLA355_H
+#define MLA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA355_ABI_VERSION 1
+
+#define MLA_D_C 512  /* latent width c_KV                         */
+#define MLA_D_R 64   /* decoupled RoPE key width k_R              */
+#define MLA_D_QK 576 /* latent row / absorbed query width         */
+#define MLA_D_K 128  /* per-head query (no-RoPE part) width       */
+#define MLA_D_V 128  /* per-head value width after o absorb       */
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARGUMENT = 1,
+    MLA_ERR_UNSUPPORTED = 2,
+    MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+    MLA_ERR_HIP = 4
+} mla_status_t;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype_t;
+
+/* Scheduling overrides and profiling hooks for mla_decode_ex.  Zero / NULL in
+ * a field means "choose automatically" / "none".  Results are the same
+ * function of the inputs for every valid setting (up to floating-point
+ * rounding order). */
+typedef struct {
+    int n_chunks;       /* token chunks the whole batch is cut into (the split-KV
+                           grid size per head group); multiple of 8, <= 65536 */
+    int heads_per_group;/* heads one workgroup scores against a shared tile:
+                           16, 32, 64 or 128 (bf16), 16 (fp32) */
+    int variant;        /* kernel variant index for the chosen head group (0 = auto) */
+    int reserved[5];    /* must be zero */
+    void* profile_events[2]; /* optional hipEvent_t pair, recorded on `stream`
+                                right before and right after the split-KV
+                                attention kernel (both or neither) */
+} mla_decode_config_t;
+
+int mla_abi_version(void);
+const char* mla_status_string(mla_status_t status);
+
+/*
+ * mla_absorb_q -- query absorption.
+ *   q_prime[b,h,0:512]   = q_nope[b,h,:] . W_UK[h]   (contracts d_k = 128)
+ *   q_prime[b,h,512:576] = q_rope[b,h,:]
+ * Glossary, section on why decode absorbs: qbar_h = q^C_h (W^UK_h)^T is a
+ * latent-width query; FlashMLA issue 16 answer: it is concatenated with the
+ * 64-wide rope query.  Layouts:
+ *   q_nope [b,h,128], w_uk [h,128,512] (row j of head h is the j-th query
+ *   dimension's weights over the 512 latent channels), q_rope [b,h,64],
+ *   q_prime [b,h,576] (written).
+ * fp32 accumulation; the result is rounded once to dtype.
+ * Errors: MLA_ERR_INVALID_ARGUMENT for a null or misaligned pointer,
+ * b <= 0, h <= 0 or an unknown dtype.
+ */
+mla_status_t mla_absorb_q(mla_dtype_t dtype, int b, int h, const void* q_nope, const void* w_uk,
+                          const void* q_rope, void* q_prime, void* stream);
+
+/*
+ * mla_decode_workspace_bytes -- bytes of device workspace mla_decode needs for
+ * this problem size.  Pure host function: it makes no HIP call and needs no GPU.
+ * Returns 0 for invalid arguments.
+ */
+size_t mla_decode_workspace_bytes(mla_dtype_t dtype, int b, int h, int t_max);
+
+/*
+ * mla_decode -- attention of every absorbed query head against the shared
+ * latent cache (the latent form of MLA decode).  For each batch row i and head
+ * j, over the first L = seqlens[i] cached rows t:
+ *   s_t      = softmax_scale * sum_{k<576} q_prime[i,j,k] * cache[i,t,k]
+ *   p_t      = exp(s_t) / sum_u exp(s_u)
+ *   out[i,j,c] = sum_t p_t * cache[i,t,c]        (c < 512; k_R is a key only)
+ *   lse[i,j] = log(sum_t exp(s_t))                (natural log)
+ * Glossary, section on why decode absorbs (scores against the cached latent,
+ * value up-projection moved after the weighted sum), and its runnable check
+ * (softmax of the summed content + RoPE score, scaled by 1/sqrt(d_k + d_r)).
+ * Layouts: q_prime [b,h,576]; cache [b,t_max,576] (row t of batch i at
+ * ((i*t_max)+t)*576); seqlens [b] int32 on the device; out [b,h,512] dtype
+ * (written); lse [b,h] fp32 (written).
+ * Tokens attended: exactly the first seqlens[i] rows, no causal mask.  A
+ * device-side seqlens value outside [0, t_max] is clamped into it.  A row with
+ * L = 0 yields out = 0 and lse = -inf.  Rows at or past L are never read.
+ * workspace: device scratch of at least mla_decode_workspace_bytes(dtype, b, h,
+ * t_max) bytes, 256-byte aligned, contents need not be initialised; it holds
+ * the split plan and the split-KV partial results.
+ * Errors (host side, before any launch): MLA_ERR_INVALID_ARGUMENT for a null
+ * or misaligned pointer, b <= 0, h <= 0, t_max < 0, b*t_max >= 2^31, unknown
+ * dtype, or softmax_scale not finite or <= 0; MLA_ERR_WORKSPACE_TOO_SMALL.
+ */
+mla_status_t mla_decode(mla_dtype_t dtype, int b, int h, int t_max, const void* q_prime,
+                        const void* cache, const int32_t* seqlens, float softmax_scale, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As mla_decode_workspace_bytes / mla_decode with explicit scheduling
+ * overrides (config may be NULL: automatic).  Additional error:
+ * MLA_ERR_UNSUPPORTED for a config field outside its documented range. */
+size_t mla_decode_workspace_bytes_ex(mla_dtype_t dtype, int b, int h, int t_max,
+                                     const mla_decode_config_t* config);
+mla_status_t mla_decode_ex(mla_dtype_t dtype, int b, int h, int t_max, const void* q_prime,
+                           const void* cache, const int32_t* seqlens, float softmax_scale,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           const mla_decode_config_t* config, void* stream);
+
+/*
+ * mla_absorb_o -- output absorption.
+ *   y[b,h,:] = o[b,h,:] . W_UV[h]   (contracts d_c = 512)
+ * Glossary, section on why decode absorbs: sum_t p_t (c_t W^UV_h) equals
+ * (sum_t p_t c_t) W^UV_h, so the up-projection runs once on the 512-wide
+ * decode output.  Layouts: o [b,h,512], w_uv [h,512,128], y [b,h,128]
+ * (written).  fp32 accumulation, one rounding to dtype.
+ * Errors: as mla_absorb_q.
+ */
+mla_status_t mla_absorb_o(mla_dtype_t dtype, int b, int h, const void* o, const void* w_uv,
+                          void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA355_H */

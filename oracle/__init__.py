@@ -94,8 +94,12 @@ class Oracle:
         lib.oracle_absorb_o.argtypes = [ci, ci, ci, ci, dp, dp, dp]
         lib.oracle_absorb_o.restype = None
         lib.oracle_abi_version.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
 
     def decode_latent(self, q_prime, cache, seqlens, scale, d_c=D_C, want_scores=False):
         """Latent form.  q_prime [b,h,d_c+d_r], cache [b,t_max,d_c+d_r], seqlens [b].

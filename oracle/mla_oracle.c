@@ -36,6 +36,7 @@
  * seqlens[b] == 0 yields out = 0, lse = -inf.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -43,6 +44,18 @@
 #define IDX3(i, j, k, n1, n2) (((size_t)(i) * (size_t)(n1) + (size_t)(j)) * (size_t)(n2) + (size_t)(k))
 
 int oracle_abi_version(void) { return 1; }
+
+/* Threads the OpenMP loops use (reported with CPU timings). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
 
 /*
  * Softmax of s[0..n) (natural exponent), written into p, returning

@@ -1,0 +1,120 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/mla355.h declares, computes workspace sizes on the host, and rejects
+bad arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla355.h")
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import head_latent_attention_decode_amd as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("mla_absorb_q", "mla_decode", "mla_absorb_o", "mla_decode_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), "missing export %s" % name
+    assert set(_declared_functions()) == set(mla.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_and_status_strings(mla):
+    assert mla.abi_version() == 1
+    assert mla.status_string(0) == "ok"
+    assert mla.status_string(3) == "workspace too small"
+
+
+def test_workspace_bytes_host_only(mla):
+    ws = mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
+    assert ws > 0 and ws % 256 == 0
+    # partial slots: at least (chunks + rows) * heads * (512 + 1) fp32 plus the plan
+    assert ws >= (8 + 64) * 128 * 513 * 4
+    n = {"n_chunks": 256, "heads_per_group": 64}
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096, n) >= (256 + 64) * 128 * 513 * 4
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 0, 128, 4096) == 0
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 4, 0, 4096) == 0
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 4, 8, -1) == 0
+    assert mla.mla_decode_workspace_bytes(torch.float32, 2, 16, 257) > 0
+    cfg = {"n_chunks": 64, "heads_per_group": 16}
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 3, 16, 100, cfg) > 0
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 3, 16, 100, {"n_chunks": 12}) == 0
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 3, 16, 100, {"heads_per_group": 48}) == 0
+
+
+# Raw C calls with fake (never dereferenced) device pointers: exactly one
+# argument is wrong in each case, so the call must fail in host validation.
+A = 0x10000  # aligned fake pointer
+SCALE = 0.0721
+
+
+def _decode(lib, dt=1, b=2, h=16, t=100, q=A, c=A, sl=A, scale=SCALE, out=A, lse=A, ws=A,
+            wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_decode(dt, b, h, t, vp(q), vp(c), vp(sl), ctypes.c_float(scale), vp(out),
+                          vp(lse), vp(ws), ctypes.c_size_t(wsb), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"q": 0}, 1), ({"c": 0}, 1), ({"sl": 0}, 1), ({"out": 0}, 1), ({"lse": 0}, 1),
+    ({"ws": 0}, 1), ({"b": 0}, 1), ({"h": -1}, 1), ({"t": -5}, 1), ({"dt": 7}, 1),
+    ({"q": A + 8}, 1), ({"c": A + 2}, 1), ({"out": A + 4}, 1), ({"ws": A + 16}, 1),
+    ({"scale": 0.0}, 1), ({"scale": -1.0}, 1), ({"scale": float("nan")}, 1),
+    ({"scale": float("inf")}, 1), ({"wsb": 1024}, 3), ({"b": 1 << 20, "t": 1 << 12}, 1),
+])
+def test_decode_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _decode(lib, **kw) == status
+
+
+def test_decode_ex_rejects_bad_config(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    vp = ctypes.c_void_p
+    for cfg in ({"n_chunks": 12}, {"n_chunks": 1 << 20}, {"heads_per_group": 24},
+                {"variant": 9}, {"reserved": (ctypes.c_int * 5)(1, 0, 0, 0, 0)}):
+        c = mla.MLAConfig()
+        for k, v in cfg.items():
+            setattr(c, k, v)
+        st = lib.mla_decode_ex(1, 2, 16, 100, vp(A), vp(A), vp(A), ctypes.c_float(SCALE), vp(A),
+                               vp(A), vp(A), ctypes.c_size_t(1 << 30), ctypes.byref(c), vp(0))
+        assert st == 2, cfg
+
+
+def test_absorb_validation(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    vp = ctypes.c_void_p
+    assert lib.mla_absorb_q(1, 4, 8, vp(0), vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_q(1, 4, 8, vp(A), vp(A + 4), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_q(1, 0, 8, vp(A), vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_q(5, 4, 8, vp(A), vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_o(1, 4, 8, vp(A), vp(0), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_o(1, 4, 0, vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_absorb_o(0, 4, 8, vp(A), vp(A), vp(A + 2), vp(0)) == 1
+
+
+def test_python_binding_checks_tensors(mla):
+    q = torch.zeros(2, 16, 576, dtype=torch.bfloat16)  # CPU tensor: rejected before any call
+    with pytest.raises(ValueError):
+        mla.mla_decode(q, torch.zeros(2, 8, 576, dtype=torch.bfloat16),
+                       torch.zeros(2, dtype=torch.int32), 0.07)
+    with pytest.raises(TypeError):
+        mla.mla_decode_workspace_bytes(torch.float16, 2, 16, 8)

@@ -1,0 +1,195 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Small cases run the oracle on every output; the full-size configurations
+(the same launch configuration the benchmark times) check sampled batch rows
+(and heads) against the oracle, plus properties that hold at any size.
+Every cache row at or past a sequence's length holds NaN, so any read past
+the end shows up as a non-finite output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import (BF16_LSE_ABS, BF16_OUT_REL, F32_REL, assert_lse, assert_out,
+                         check_decode, to_np)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = workloads.SCALE
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_latent_attention_decode_amd as m
+    return m
+
+
+def _run(mla, w, config=None):
+    out, lse = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale, config=config)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# ---------------------------------------------------------------- fp32 (tiny config)
+
+def test_tiny_fp32_pipeline(mla):
+    w = workloads.make(1, device="cuda")
+    # q absorb against the oracle's absorb
+    qp_gpu = mla.mla_absorb_q(w.q_nope, w.w_uk, w.q_rope)
+    qp_ref = oracle.absorb_q(w.q_nope.cpu(), w.w_uk.cpu(), w.q_rope.cpu())
+    torch.cuda.synchronize()
+    assert_out(to_np(qp_gpu), qp_ref, F32_REL, "q'")
+    # decode fed the oracle's q' (never the HIP path's)
+    qp_in = torch.from_numpy(qp_ref).to(torch.float32).cuda()
+    ref_out, ref_lse = oracle.decode_latent(qp_in.cpu(), w.cache.cpu(), w.seqlens.cpu(), w.scale)
+    for cfg in (None, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
+        out, lse = mla.mla_decode(qp_in, w.cache, w.seqlens, w.scale, config=cfg)
+        torch.cuda.synchronize()
+        assert_out(to_np(out), ref_out, F32_REL, "out %s" % cfg)
+        assert_out(to_np(lse), ref_lse, F32_REL, "lse %s" % cfg)
+    # end to end against the expanded (un-absorbed) form
+    bufs = mla.alloc_step(w.b, w.h, w.t_max, torch.float32)
+    y = mla.mla_step(w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.cache, w.seqlens, w.scale, bufs)
+    torch.cuda.synchronize()
+    y_ref, lse_x = oracle.decode_unabsorbed(w.q_nope.cpu(), w.q_rope.cpu(), w.w_uk.cpu(),
+                                            w.w_uv.cpu(), w.cache.cpu(), w.seqlens.cpu(), w.scale)
+    assert_out(to_np(y), y_ref, F32_REL, "y")
+    assert_out(to_np(bufs.lse), lse_x, F32_REL, "lse vs expanded form")
+
+
+# ---------------------------------------------------------------- bf16, small, every output
+
+EDGE_LENS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 0, 700]
+
+BF16_CASES = [
+    # (h, config)
+    (1, None), (3, None), (16, None), (16, {"heads_per_group": 16, "variant": 2}),
+    (32, None), (32, {"heads_per_group": 32, "variant": 2}), (64, None),
+    (64, {"heads_per_group": 64, "variant": 2}), (128, None),
+    (128, {"heads_per_group": 128, "variant": 2}), (128, {"heads_per_group": 64}),
+    (128, {"heads_per_group": 16}), (40, {"heads_per_group": 16}),
+]
+
+
+@pytest.mark.parametrize("h,cfg", BF16_CASES, ids=[f"h{h}-{c}" for h, c in BF16_CASES])
+def test_bf16_edges_every_output(mla, h, cfg):
+    w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=100 + h, device="cuda")
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}):
+        c = dict(cfg or {})
+        c.update(extra)
+        out, lse = _run(mla, w, c or None)
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
+        # empty row: out = 0, lse = -inf
+        assert torch.all(out[EDGE_LENS.index(0)] == 0)
+        assert torch.all(torch.isneginf(lse[EDGE_LENS.index(0)]))
+
+
+def test_bf16_split_invariance_and_determinism(mla):
+    w = workloads.make_custom(5, 128, [3000, 17, 4096, 1, 2500], seed=7, device="cuda")
+    outs = []
+    for n in (8, 16, 64, 256, 1024):
+        out, lse = _run(mla, w, {"n_chunks": n})
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
+        outs.append((out.clone(), lse.clone()))
+        out2, lse2 = _run(mla, w, {"n_chunks": n})
+        assert torch.equal(out, out2) and torch.equal(lse, lse2), "not deterministic"
+    # different schedules agree with each other to the same tolerance
+    ref_o, ref_l = to_np(outs[0][0]), to_np(outs[0][1])
+    for o, l in outs[1:]:
+        assert_out(to_np(o), ref_o, BF16_OUT_REL)
+        assert_lse(to_np(l), ref_l, BF16_LSE_ABS)
+
+
+def test_bf16_closed_forms(mla):
+    # zero query: lse = ln L exactly (up to fp32), out = mean of the latent rows
+    lens = [1, 77, 1024]
+    w = workloads.make_custom(3, 16, lens, seed=9, device="cuda")
+    w.q_prime.zero_()
+    out, lse = _run(mla, w)
+    for i, L in enumerate(lens):
+        np.testing.assert_allclose(to_np(lse[i]), math.log(L), atol=1e-5)
+        mean = to_np(w.cache[i, :L, :512].float()).mean(0)
+        assert_out(to_np(out[i]), np.broadcast_to(mean, (16, 512)), BF16_OUT_REL)
+    # constant score shift: cache[..., 575] = 1, q'[..., 575] += delta
+    w = workloads.make_custom(2, 32, [500, 333], seed=10, device="cuda")
+    w.cache[:, :, 575] = 1.0
+    workloads.poison_tail(w.cache, w.seqlens)
+    out0, lse0 = _run(mla, w)
+    q575_before = w.q_prime[:, :, 575].float().clone()
+    w.q_prime[:, :, 575] += 8.0
+    out1, lse1 = _run(mla, w)
+    # the bf16 addition rounds, so each head's actual shift is read back exactly
+    shift = (w.q_prime[:, :, 575].float() - q575_before).cpu().double().numpy()
+    assert_out(to_np(out1), to_np(out0), BF16_OUT_REL, "out under shift")
+    np.testing.assert_allclose(to_np(lse1 - lse0), SCALE * shift, atol=2e-3)
+
+
+# ---------------------------------------------------------------- absorbs, bf16
+
+def test_absorbs_bf16(mla):
+    q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(64, 128, device="cuda")
+    qp = mla.mla_absorb_q(q_nope, w_uk, q_rope)
+    o = torch.randn(64, 128, 512, device="cuda").to(torch.bfloat16)
+    y = mla.mla_absorb_o(o, w_uv)
+    torch.cuda.synchronize()
+    ref_q = oracle.absorb_q(q_nope.cpu(), w_uk.cpu(), q_rope.cpu())
+    assert_out(to_np(qp), ref_q, BF16_OUT_REL, "q'")
+    np.testing.assert_array_equal(to_np(qp[..., 512:]), to_np(q_rope))
+    ref_y = oracle.absorb_o(o.cpu(), w_uv.cpu())
+    assert_out(to_np(y), ref_y, BF16_OUT_REL, "y")
+
+
+# ---------------------------------------------------------------- full-size configurations
+
+def _full(mla, cid, rows):
+    w = workloads.make(cid, device="cuda")
+    out, lse = _run(mla, w)
+    assert torch.isfinite(out).all(), "non-finite output (read past a sequence end?)"
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, rows)
+    return w, out, lse
+
+
+def test_full_dsv3_decode_b64_h128_T4096(mla):
+    _full(mla, 2, [0, 17, 42, 63])
+
+
+def test_full_few_heads_b128_h16_T8192(mla):
+    _full(mla, 3, [0, 1, 77, 127])
+
+
+def test_full_ragged_b132_h128(mla):
+    w = workloads.make(4, device="cuda")
+    lens = w.seqlens.cpu().tolist()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 131, 66})
+    out, lse = _run(mla, w)
+    assert torch.isfinite(out).all()
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, rows)
+
+
+def test_full_long_context_end_to_end(mla):
+    w = workloads.make(5, device="cuda")
+    # absorbs in full
+    qp_gpu = mla.mla_absorb_q(w.q_nope, w.w_uk, w.q_rope)
+    torch.cuda.synchronize()
+    qp_ref = oracle.absorb_q(w.q_nope.cpu(), w.w_uk.cpu(), w.q_rope.cpu())
+    assert_out(to_np(qp_gpu), qp_ref, BF16_OUT_REL, "q'")
+    # decode fed the oracle's q' rounded to bf16; heads sampled
+    qp_in = torch.from_numpy(qp_ref).to(torch.bfloat16).cuda()
+    out, lse = mla.mla_decode(qp_in, w.cache, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    heads = [0, 1, 63, 64, 126, 127]
+    check_decode(qp_in, w.cache, w.seqlens, w.scale, out, lse, range(4), heads)
+    # end to end (absorb -> decode -> absorb) against the oracle's own pipeline
+    bufs = mla.alloc_step(w.b, w.h, w.t_max)
+    y = mla.mla_step(w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.cache, w.seqlens, w.scale, bufs)
+    torch.cuda.synchronize()
+    ref_out, _ = oracle.decode_latent(torch.from_numpy(qp_ref)[:, heads], w.cache.cpu(),
+                                      w.seqlens.cpu(), w.scale)
+    ref_y = oracle.absorb_o(ref_out, w.w_uv.cpu()[heads])
+    assert_out(to_np(y[:, heads]), ref_y, BF16_OUT_REL, "y")
