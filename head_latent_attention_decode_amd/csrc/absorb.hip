@@ -6,11 +6,14 @@
 //             query into the 576-wide attention input;
 //   o absorb: (sum_t p_t c_t) W^UV_h, the value up-projection applied once to
 //             the 512-wide attention output.
-// Both are weight-read bound at decode batch sizes (each head's 128 x 512
-// weight block is used by only b query rows), so they run on the vector ALU
-// with fp32 accumulation: one workgroup per (head, block of 16 batch rows)
-// streams that head's weights once with coalesced vector loads and keeps the
-// 16 rows' inputs in LDS.
+// Both are per-head products with a 128 x 512 weight block used by only b
+// query rows, so they are weight-read bound at small b.  bf16: one workgroup
+// per (head, 64 output columns) stages that weight slab in LDS once, reads
+// it transposed (ds_read_b64_tr_b16) as the A operand of
+// v_mfma_f32_16x16x32_bf16, and streams the b input rows as the B operand
+// (contraction dimension contiguous in memory), fp32 accumulation.  fp32: the
+// vector-ALU kernels below (IEEE fp32 FMAs), one workgroup per (head, block of
+// 16 batch rows).
 #include "mla355_internal.h"
 
 namespace mla355 {
@@ -75,11 +78,14 @@ __global__ __launch_bounds__(128) void absorb_q_kernel(int b, int h, const T* __
             acc[rr][3] = fmaf(q, w3, acc[rr][3]);
         }
     }
-    for (int rr = 0; rr < nrows; ++rr) {
-        v4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[rr][e]);
-        *(v4*)(q_prime + ((size_t)(r0 + rr) * h + head) * kDqk + 4 * t) = o;
+    for (int rr = 0; rr < kRows; ++rr) {
+        if (rr < nrows) {
+            v4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[rr][e]);
+            *(v4*)(q_prime + ((size_t)(r0 + rr) * h + head) * kDqk + 4 * t) = o;
+        }
     }
     for (int i = t; i < nrows * kDr; i += 128) {
         const int rr = i / kDr, j = i % kDr;
@@ -114,7 +120,102 @@ __global__ __launch_bounds__(128) void absorb_o_kernel(int b, int h, const T* __
 #pragma unroll
         for (int rr = 0; rr < kRows; ++rr) acc[rr] = fmaf(os[rr][c], wv, acc[rr]);
     }
-    for (int rr = 0; rr < nrows; ++rr) y[((size_t)(r0 + rr) * h + head) * kDv + t] = from_f32<T>(acc[rr]);
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr)
+        if (rr < nrows) y[((size_t)(r0 + rr) * h + head) * kDv + t] = from_f32<T>(acc[rr]);
+}
+
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// Weight slab [KD][64] bf16 in LDS, 128-byte rows.  16-byte chunk c of row r is
+// stored at c ^ (2 * f(r)), f(r) = ((r >> 1) & 1) | (((r >> 3) & 1) << 1), so the
+// transposed reads of 4-row groups spread over distinct 32-byte bank windows.
+__device__ __forceinline__ int slab_off(int r, int c)
+{
+    const int f = ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+    return r * 128 + ((c ^ (2 * f)) << 4);
+}
+
+// Y^T[n, m] = sum_k W[h][k][n] X[m][h][k] for 64 columns n0.. of head h.
+//   W  [H][KD][ND] (n contiguous)      X  row m of head h at x + m*x_rs + h*KD
+//   Y  row m of head h at y + m*y_rs + h*y_hs + n
+// 4 waves; wave w owns columns n0 + 16w .. +15 (MFMA A rows); batch rows are
+// the MFMA B columns, 16 per block.  When rope != nullptr (q absorb), the
+// workgroups of column block 0 also copy rope[m][h][0:64] to y[...][ND:ND+64].
+template <int KD, int ND>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __bf16* __restrict__ x,
+                                                          long x_rs, const __bf16* __restrict__ w,
+                                                          __bf16* __restrict__ y, long y_rs, int y_hs,
+                                                          const __bf16* __restrict__ rope)
+{
+    constexpr int NB = ND / 64;
+    constexpr int KSTEPS = KD / 32;
+    __shared__ __attribute__((aligned(16))) unsigned char slab[KD * 128];
+    const int h = blockIdx.x / NB;
+    const int n0 = (blockIdx.x % NB) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // stage W[h][:, n0:n0+64] (KD rows x 8 chunks of 16 B)
+    const __bf16* wh = w + (size_t)h * KD * ND + n0;
+#pragma unroll 4
+    for (int i = tid; i < KD * 8; i += 256) {
+        const int r = i >> 3, c = i & 7;
+        const bf16x8_t v = *(const bf16x8_t*)(wh + (size_t)r * ND + c * 8);
+        *(LDS_AS bf16x8_t*)((LDS_AS unsigned char*)slab + slab_off(r, c)) = v;
+    }
+    if (rope != nullptr && n0 == 0) {
+        for (int i = tid; i < M * 8; i += 256) {
+            const int m = i >> 3, c = i & 7;
+            const bf16x8_t v = *(const bf16x8_t*)(rope + ((size_t)m * H + h) * 64 + c * 8);
+            *(bf16x8_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + ND + c * 8) = v;
+        }
+    }
+    __syncthreads();
+
+    // A operand (W^T rows n, k-slots g*8 .. +7) for every k step, read once.
+    // tr16 mapping: source lane s of a 16-lane group supplies row k0 + g*8 + s/4
+    // (+4 for the upper half), columns 4*(s%4) .. +3 of the wave's 16 columns.
+    const int g = lane >> 4, s = lane & 15;
+    const int col = wave * 16 + 4 * (s & 3);
+    bf16x8_t a[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int r0 = ks * 32 + g * 8 + (s >> 2);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)((LDS_AS unsigned char*)slab + slab_off(r0, col >> 3) + (col & 7) * 2));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)((LDS_AS unsigned char*)slab + slab_off(r0 + 4, col >> 3) + (col & 7) * 2));
+        a[ks] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // B operand: X rows (batch rows m = mb*16 + s), k-slots g*8 .. +7.
+    for (int mb = 0; mb * 16 < M; ++mb) {
+        const int m = mb * 16 + s;
+        const bool ok = m < M;
+        const __bf16* xr = x + (size_t)(ok ? m : 0) * x_rs + (size_t)h * KD + g * 8;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            bf16x8_t b = *(const bf16x8_t*)(xr + ks * 32);
+            if (!ok) b = (bf16x8_t){};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc, 0, 0, 0);
+        }
+        // acc[i]: output column n0 + 16*wave + g*4 + i of batch row m
+        if (ok) {
+            bf16x4_t o;
+            o[0] = (__bf16)acc[0];
+            o[1] = (__bf16)acc[1];
+            o[2] = (__bf16)acc[2];
+            o[3] = (__bf16)acc[3];
+            *(bf16x4_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + wave * 16 + g * 4) = o;
+        }
+    }
 }
 
 }  // namespace
@@ -124,9 +225,9 @@ hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const vo
 {
     const unsigned grid = (unsigned)h * (unsigned)((b + kRows - 1) / kRows);
     if (bf16)
-        absorb_q_kernel<__bf16><<<grid, 128, 0, stream>>>(b, h, (const __bf16*)q_nope,
-                                                          (const __bf16*)w_uk, (const __bf16*)q_rope,
-                                                          (__bf16*)q_prime);
+        absorb_mfma_kernel<kDk, kDc><<<h * (kDc / 64), 256, 0, stream>>>(
+            b, h, (const __bf16*)q_nope, (long)h * kDk, (const __bf16*)w_uk, (__bf16*)q_prime,
+            (long)h * kDqk, kDqk, (const __bf16*)q_rope);
     else
         absorb_q_kernel<float><<<grid, 128, 0, stream>>>(b, h, (const float*)q_nope,
                                                          (const float*)w_uk, (const float*)q_rope,
@@ -139,8 +240,9 @@ hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w
 {
     const unsigned grid = (unsigned)h * (unsigned)((b + kRows - 1) / kRows);
     if (bf16)
-        absorb_o_kernel<__bf16><<<grid, 128, 0, stream>>>(b, h, (const __bf16*)o,
-                                                          (const __bf16*)w_uv, (__bf16*)y);
+        absorb_mfma_kernel<kDc, kDv><<<h * (kDv / 64), 256, 0, stream>>>(
+            b, h, (const __bf16*)o, (long)h * kDc, (const __bf16*)w_uv, (__bf16*)y, (long)h * kDv,
+            kDv, nullptr);
     else
         absorb_o_kernel<float><<<grid, 128, 0, stream>>>(b, h, (const float*)o,
                                                          (const float*)w_uv, (float*)y);

@@ -48,9 +48,15 @@ mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* c
         if (cfg && cfg->variant != 0) return MLA_ERR_UNSUPPORTED;
         s->min_chunk = 16;
     } else {
+        // <= 16 heads: single-wave 16-head workgroups (memory-bound regime);
+        // more heads: paired-wave 32x32-MFMA workgroups of 64 heads.
         int hpg = h <= 16 ? 16 : h <= 32 ? 32 : 64;
-        if (cfg && cfg->heads_per_group != 0) hpg = cfg->heads_per_group;
-        const int variant = (cfg && cfg->variant != 0) ? cfg->variant : 1;
+        int def_variant = h <= 16 ? 2 : h <= 32 ? 1 : 3;
+        if (cfg && cfg->heads_per_group != 0) {
+            hpg = cfg->heads_per_group;
+            def_variant = 1;
+        }
+        const int variant = (cfg && cfg->variant != 0) ? cfg->variant : def_variant;
         if (!bf16_variant_exists(hpg, variant)) return MLA_ERR_UNSUPPORTED;
         s->hpg = hpg;
         s->variant = variant;

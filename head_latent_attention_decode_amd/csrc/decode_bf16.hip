@@ -79,6 +79,19 @@ __device__ __forceinline__ void wg_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier for data exchanged through ordinary LDS stores (not DMA): waits for
+// this wave's LDS accesses (lgkmcnt) only.  A release fence on LDS would also
+// wait for every DMA still landing in other stages (the compiler counts those
+// as LDS writes), which would serialise the tile prefetch with compute.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_exchange_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // One LDS array per pipeline stage.  Distinct objects let the compiler prove
 // that reads of one stage do not alias DMA still landing in another, so it
 // does not insert conservative vmcnt(0) waits before them.
@@ -322,32 +335,47 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
                 wait_vmcnt<(STAGES > 2 ? (STAGES - 2) * T::LOADS : 0)>();
             else
                 wait_vmcnt<0>();
-            wg_barrier();  // tile `it` visible to all waves; stage of tile it-1 free
+            // DMA of tile `it` complete (vmcnt above); after the barrier every wave
+            // sees it, and every wave has consumed its reads of tile it-1.
+            lds_exchange_barrier();
             if (it + STAGES - 1 < n_tiles) issue_tile(IC<(S + STAGES - 1) % STAGES>{}, it + STAGES - 1);
 
             lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
             const int tvalid = seg_len - it * T::N - tok0;  // valid tokens for this wave (may be <= 0)
 
             // ---- S^T = K . Q^T -------------------------------------------------
-            acc_t sacc[T::SBLK];
+            // K fragments stream through a small register ring, PF steps ahead
+            // of the MFMA that consumes them; the scheduling fence after every
+            // step keeps the compiler from hoisting all of a tile's LDS reads
+            // (which would exhaust the register file).  Two accumulator chains
+            // per S block (even / odd k steps) keep dependent MFMAs apart.
+            constexpr int NSTEP = T::KSTEPS * T::SBLK;
+            constexpr int PF = 4;
+            auto k_addr = [&](int idx) -> const lds_byte* {
+                const int ks = idx / T::SBLK, sb = idx % T::SBLK;
+                if (ks < T::KSTEPS_A) return tb + koffA[ks % NQA] + (ks / NQA) * 256 + sb * WH * 1024;
+                return tb + koffB[ks - T::KSTEPS_A] + sb * WH * 128;
+            };
+            acc_t sacc[T::SBLK][2];
 #pragma unroll
-            for (int sb = 0; sb < T::SBLK; ++sb) sacc[sb] = (acc_t){};
+            for (int sb = 0; sb < T::SBLK; ++sb) sacc[sb][0] = sacc[sb][1] = (acc_t){};
+            bf16x8_t kring[PF];
 #pragma unroll
-            for (int ks = 0; ks < T::KSTEPS; ++ks) {
+            for (int i = 0; i < PF; ++i) kring[i] = *(const LDS_AS bf16x8_t*)k_addr(i);
 #pragma unroll
-                for (int sb = 0; sb < T::SBLK; ++sb) {
-                    const lds_byte* a;
-                    if (ks < T::KSTEPS_A)
-                        a = tb + koffA[ks % NQA] + (ks / NQA) * 256 + sb * WH * 1024;
-                    else
-                        a = tb + koffB[ks - T::KSTEPS_A] + sb * WH * 128;
-                    const bf16x8_t kf = *(const LDS_AS bf16x8_t*)a;
-                    sacc[sb] = M::mma(kf, qf[ks], sacc[sb]);
-                }
+            for (int idx = 0; idx < NSTEP; ++idx) {
+                const int ks = idx / T::SBLK, sb = idx % T::SBLK;
+                const bf16x8_t kf = kring[idx % PF];
+                if (idx + PF < NSTEP) kring[idx % PF] = *(const LDS_AS bf16x8_t*)k_addr(idx + PF);
+                sacc[sb][ks & 1] = M::mma(kf, qf[ks], sacc[sb][ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            acc_t sfin[T::SBLK];
+#pragma unroll
+            for (int sb = 0; sb < T::SBLK; ++sb) sfin[sb] = sacc[sb][0] + sacc[sb][1];
 
             // ---- online softmax (lane-local head) ------------------------------
-            // sacc[sb][i] is the score of token tok0 + sb*WH + toff(i), head hl.
+            // sfin[sb][i] is the score of token tok0 + sb*WH + toff(i), head hl.
             float tmax = -INFINITY;
             const bool full = tvalid >= NT;
 #pragma unroll
@@ -355,9 +383,9 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
 #pragma unroll
                 for (int i = 0; i < M::kAcc; ++i) {
                     const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
-                    float v = sacc[sb][i] * p.scale_log2;
+                    float v = sfin[sb][i] * p.scale_log2;
                     if (!full && sb * WH + toff >= tvalid) v = -INFINITY;
-                    sacc[sb][i] = v;
+                    sfin[sb][i] = v;
                     tmax = fmaxf(tmax, v);
                 }
             }
@@ -380,7 +408,7 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             for (int sb = 0; sb < T::SBLK; ++sb) {
 #pragma unroll
                 for (int i = 0; i < M::kAcc; ++i) {
-                    const float e = exp2_fast(sacc[sb][i] - m_run);
+                    const float e = exp2_fast(sfin[sb][i] - m_run);
                     l_run += e;
                     if (WH == 16)
                         pb[sb >> 1][(sb & 1) * 4 + i] = (__bf16)e;
@@ -391,22 +419,31 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
 
             // ---- O^T += V^T . P^T ------------------------------------------------
             // MFMA u covers 32 (WH=16) or 16 (WH=32) tokens starting at tok0 + u*TPU.
+            // Transposed V fragments stream through a register ring like K above.
             constexpr int TPU = (WH == 16) ? 32 : 16;
+            constexpr int NPV = NPB * T::MBLK;
+            constexpr int PFV = 4;
+            auto v_frag = [&](int idx) -> bf16x8_t {
+                const int u = idx / T::MBLK, mb = idx % T::MBLK;
+                const int q = mb % NQV;
+                const int blk = (mb / NQV) * 256 + u * TPU * 1024;
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS i16x4_t*)(tb + voff0[q] + blk));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS i16x4_t*)(tb + (WH == 16 ? voff0[q] + 16 * 1024 : voff1[q]) + blk));
+                return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                               __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8_t vring[PFV];
 #pragma unroll
-            for (int u = 0; u < NPB; ++u) {
+            for (int i = 0; i < PFV; ++i) vring[i] = v_frag(i);
 #pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb) {
-                    const int q = mb % NQV;
-                    const int blk = (mb / NQV) * 256 + u * TPU * 1024;
-                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4_t*)(tb + voff0[q] + blk));
-                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4_t*)(tb + (WH == 16 ? voff0[q] + 16 * 1024 : voff1[q]) + blk));
-                    const bf16x4_t lo4 = __builtin_bit_cast(bf16x4_t, lo);
-                    const bf16x4_t hi4 = __builtin_bit_cast(bf16x4_t, hi);
-                    const bf16x8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[mb] = M::mma(a, pb[u], o[mb]);
-                }
+            for (int idx = 0; idx < NPV; ++idx) {
+                const int u = idx / T::MBLK, mb = idx % T::MBLK;
+                const bf16x8_t a = vring[idx % PFV];
+                if (idx + PFV < NPV) vring[idx % PFV] = v_frag(idx + PFV);
+                o[mb] = M::mma(a, pb[u], o[mb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -506,6 +543,435 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Paired-wave, software-pipelined variant for many heads
+// (v_mfma_f32_32x32x16_bf16 throughout).
+//
+// A wave that owned 32 heads outright would hold 144 VGPRs of queries and
+// 256 accumulator registers of output, leaving no room for the score tile.
+// Here the two waves of a pair share 32 heads:
+//   * scores: wave q (0/1) contracts half of the 576 latent dims -- region-A
+//     chunks [32q, 32q+32) (latent columns 256q .. 256q+255) and region-B
+//     chunks [4q, 4q+4) (rope columns 32q .. 32q+31) -- so it keeps only 72
+//     VGPRs of queries.  The two fp32 partial score tiles are exchanged
+//     through LDS and summed (fp addition is commutative, so both waves derive
+//     bit-identical softmax state);
+//   * weighted sum: wave q accumulates latent columns 256q .. 256q+255 only
+//     (128 accumulator registers).
+// With one wave per SIMD, the matrix unit would idle while the wave does
+// softmax arithmetic and LDS exchange, so each iteration overlaps work of two
+// tiles: while the score MFMAs of tile i+1 run, the vector ALU computes the
+// softmax of tile i; while the weighted-sum MFMAs of tile i run, the partial
+// scores of tile i+1 go to the partner.  Tiles are 32 tokens; a STAGES-deep
+// ring of LDS stages is refilled by DMA as soon as every wave has finished a
+// tile (two tiles are in use at any time, STAGES-2 are in flight).
+// ---------------------------------------------------------------------------
+template <int P, int STAGES>
+struct PairTiling {
+    static constexpr int NW = 2 * P;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int HG = 32 * P;
+    static constexpr int N = 32;
+    static constexpr int A_BYTES = N * 1024;
+    static constexpr int TILE_BYTES = N * kRowBytesBf16;
+    static constexpr int XBUF_BYTES = NW * 64 * 16 * 4;   // one 32x32 fp32 tile per wave
+    static constexpr int LOADS_A = N / NW;
+    static constexpr int GROUPS_B = N / 8;
+    static constexpr int LOADS_B_MAX = (GROUPS_B + NW - 1) / NW;
+    static constexpr int LOADS = LOADS_A + LOADS_B_MAX;
+    static constexpr int KA = 16;   // k steps (of 16) in region A per wave
+    static constexpr int KB = 2;    // k steps in region B per wave
+    static constexpr int KS = KA + KB;
+    static constexpr int MBLK = 8;  // 32-column output blocks per wave
+    static_assert(N % NW == 0, "region A rows split evenly over waves");
+    static_assert(STAGES >= 3 && STAGES <= 4, "pipeline depth");
+    static_assert(GROUPS_B % NW == 0, "exact vmcnt accounting needs even B split");
+    static_assert(STAGES * TILE_BYTES + XBUF_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((STAGES - 1) * LOADS <= 63, "vmcnt range");
+};
+
+template <int P, int STAGES>
+__global__ __launch_bounds__(P * 128) void decode_pair_kernel(DecodeParams p)
+{
+    using T = PairTiling<P, STAGES>;
+    using M = Mfma<32>;
+    typedef f32x16_t acc_t;
+
+    const int lane = threadIdx.x & 63;
+    // wave index is uniform: keep it (and all row/DMA arithmetic built on it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pr = wave >> 1;          // pair inside the workgroup
+    const int q = wave & 1;            // contraction half / output-column half
+    const int hl = lane & 31;          // head inside the pair's 32
+    const int grp = lane >> 5;         // k-slot group (0/1)
+
+    int k, hg;
+    if (p.n_hg == 1) {
+        k = blockIdx.x;
+        hg = 0;
+    } else {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        k = (slot / p.n_hg) * 8 + xcd;
+        hg = slot % p.n_hg;
+    }
+    const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
+    const int total = p.plan[0];
+    const int chunk = p.plan[1];
+    int r = pv.chunk_row()[k];
+    if (r < 0) return;
+    int pos = k * chunk;
+    const int end = pos + min(chunk, total - pos);
+
+    const __bf16* __restrict__ qg = (const __bf16*)p.q;
+    const unsigned char* __restrict__ cg = (const unsigned char*)p.cache;
+    const int head = hg * T::HG + pr * 32 + hl;
+    const bool head_ok = head < p.h;
+    lds_byte* const xbuf = stage_lds<T::XBUF_BYTES, 7>();
+    const float c2 = p.scale_log2;
+
+    // ---- per-lane LDS offsets --------------------------------------------
+    // K reads: token row rr = lane & 31, k step j of region A -> logical chunk
+    // 32q + 2j + grp;  region B step j -> chunk 4q + 2j + grp.
+    const int rr = lane & 31;
+    int koffA[8], koffB[T::KB];
+    {
+        const int x = M::xa(rr & 15);
+        const int xbv = xb(rr & 15);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) koffA[j] = rr * 1024 + (((2 * j + grp) ^ x) << 4) + q * 512;
+#pragma unroll
+        for (int j = 0; j < T::KB; ++j) koffB[j] = T::A_BYTES + rr * 128 + (((4 * q + 2 * j + grp) ^ xbv) << 4);
+    }
+    // V^T reads (transposed, region A): rows u*16 + grp*4 + (lane&15)/4 (+8),
+    // columns 256q + 32mb + 16*((lane>>4)&1) + 4*(lane&3).
+    int voff0[4], voff1[4];
+    {
+        const int row0 = (lane >> 5) * 4 + ((lane & 15) >> 2);
+        const int x0 = M::xa(row0 & 15), x1 = M::xa((row0 + 8) & 15);
+        const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            voff0[j] = row0 * 1024 + (((4 * j + cc) ^ x0) << 4) + ((lane & 1) << 3) + q * 512;
+            voff1[j] = (row0 + 8) * 1024 + (((4 * j + cc) ^ x1) << 4) + ((lane & 1) << 3) + q * 512;
+        }
+    }
+
+    while (true) {
+        const int row_lo = pv.cu()[r];
+        const int row_hi = pv.cu()[r + 1];
+        const int seg_end = min(end, row_hi);
+        const int seg_a = pos - row_lo;
+        const int seg_len = seg_end - pos;
+        const int split_j = k - row_lo / chunk;
+        const bool final_out = pv.nsplit()[r] == 1;
+        const int slot = pv.base()[r] + split_j;
+        const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
+        const int n_tiles = (seg_len + T::N - 1) / T::N;
+
+        // Queries for this wave's contraction half: B operand, lane -> head hl,
+        // k-slots grp*8 .. +7 of each 16-wide step.
+        bf16x8_t qf[T::KS];
+        {
+            const bf16x8_t* qrow =
+                (const bf16x8_t*)(qg + ((size_t)r * p.h + (head_ok ? head : 0)) * kDqk);
+#pragma unroll
+            for (int j = 0; j < T::KA; ++j) {
+                bf16x8_t v = qrow[(256 * q + 16 * j) / 8 + grp];
+                if (!head_ok) v = (bf16x8_t){};
+                qf[j] = v;
+            }
+#pragma unroll
+            for (int j = 0; j < T::KB; ++j) {
+                bf16x8_t v = qrow[(512 + 32 * q + 16 * j) / 8 + grp];
+                if (!head_ok) v = (bf16x8_t){};
+                qf[T::KA + j] = v;
+            }
+        }
+
+        auto issue_tile = [&](auto SC, int tile) {
+            const int t0 = tile * T::N;
+            const int last = min(T::N, seg_len - t0) - 1;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(seg_base + (size_t)t0 * kRowBytesBf16), (short)0,
+                (last + 1) * kRowBytesBf16, kBufferFlags);
+            lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
+#pragma unroll
+            for (int j = 0; j < T::LOADS_A; ++j) {
+                const int row = wave + j * T::NW;
+                const int srow = min(row, last);
+                const unsigned voff = (unsigned)((lane ^ M::xa(row & 15)) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (LDS_AS void*)(st + row * 1024), 16, voff,
+                    __builtin_amdgcn_readfirstlane(srow * kRowBytesBf16), 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < T::LOADS_B_MAX; ++j) {
+                const int gb = wave + j * T::NW;
+                const int row = gb * 8 + (lane >> 3);
+                const int srow = min(row, last);
+                const int lc = (lane & 7) ^ xb(row & 15);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (LDS_AS void*)(st + T::A_BYTES + gb * 1024), 16,
+                    (unsigned)(srow * kRowBytesBf16 + 1024 + lc * 16), 0, 0, 0);
+            }
+        };
+        // Wait until tile `t` has landed: tiles issued after it are t+1 ..
+        // min(t+STAGES-2, n_tiles-1) (the ring never holds more than that).
+        auto wait_tile = [&](int t) {
+            const int after = min(STAGES - 2, n_tiles - 1 - t);
+            if (after >= 2)
+                wait_vmcnt<(STAGES > 3 ? 2 : 0) * T::LOADS>();
+            else if (after == 1)
+                wait_vmcnt<T::LOADS>();
+            else
+                wait_vmcnt<0>();
+        };
+
+        acc_t o[T::MBLK];
+#pragma unroll
+        for (int mb = 0; mb < T::MBLK; ++mb) o[mb] = (acc_t){};
+        float m_run = kNegBig;
+        float l_run = 0.f;
+
+        // K fragment j of the tile in stage SB.
+        auto k_frag = [&](lds_byte* tb, int j) -> bf16x8_t {
+            const lds_byte* a = (j < T::KA) ? tb + koffA[j % 8] + (j / 8) * 256 : tb + koffB[j - T::KA];
+            return *(const LDS_AS bf16x8_t*)a;
+        };
+        // Transposed V fragment idx (u = idx / MBLK token half, mb = idx % MBLK).
+        auto v_frag = [&](lds_byte* tb, int idx) -> bf16x8_t {
+            const int u = idx / T::MBLK, mb = idx % T::MBLK;
+            const int blk = (mb / 4) * 256 + u * 16 * 1024;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff0[mb % 4] + blk));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff1[mb % 4] + blk));
+            return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        // Exchange this wave's partial score tile with the partner's: returns the sum.
+        auto exchange = [&](const acc_t& part) -> acc_t {
+            LDS_AS f32x4_t* mine = (LDS_AS f32x4_t*)(xbuf + wave * 4096);
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                mine[i4 * 64 + lane] = (f32x4_t){part[4 * i4], part[4 * i4 + 1], part[4 * i4 + 2], part[4 * i4 + 3]};
+            lds_exchange_barrier();
+            const LDS_AS f32x4_t* other = (const LDS_AS f32x4_t*)(xbuf + (wave ^ 1) * 4096);
+            f32x4_t ov[4];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) ov[i4] = other[i4 * 64 + lane];
+            acc_t sum;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum[i] = part[i] + ov[i >> 2][i & 3];
+            return sum;
+        };
+
+        // Softmax pieces on the (raw) score tile sc of tile t; see the header.
+        // sc[i]: token (i/4)*8 + grp*4 + i%4 of the tile, head hl.
+        float sm_tmax = 0.f;
+        auto sm_max = [&](acc_t& sc, int t) {
+            const int tvalid = __builtin_amdgcn_readfirstlane(seg_len - t * T::N);
+            if (tvalid < T::N) {  // tail tile: scores of missing tokens -> -inf
+                // token of entry i is (i/4)*8 + i%4 + 4*grp: compare the constant
+                // part against one per-lane limit
+                const int lim = tvalid - 4 * grp;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -INFINITY;
+            }
+            float tm = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+            for (int i = 3; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+            // the head's other lane group is lane ^ 32
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, tm),
+                                                             __builtin_bit_cast(unsigned, tm), false, false);
+            sm_tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
+        };
+        auto sm_rescale = [&]() {
+            const float m_new = fmaxf(m_run, sm_tmax);
+            if (__any(m_new > m_run + kRescaleThreshold)) {
+                const float alpha = exp2_fast(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb) o[mb] *= alpha;
+                m_run = m_new;
+            }
+        };
+        auto sm_exp = [&](const acc_t& sc, bf16x8_t* pb, int i0) {
+#pragma unroll
+            for (int i = i0; i < i0 + 4; ++i) {
+                const float e = exp2_fast(__builtin_fmaf(sc[i], c2, -m_run));
+                l_run += e;
+                pb[i >> 3][i & 7] = (__bf16)e;
+            }
+        };
+
+        // ---- prologue: fill the ring, scores of tile 0 ----------------------
+        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
+        if (1 < n_tiles) issue_tile(IC<1>{}, 1);
+        if (2 < n_tiles) issue_tile(IC<2>{}, 2);
+        if (STAGES > 3 && 3 < n_tiles) issue_tile(IC<(STAGES > 3 ? 3 : 0)>{}, 3);
+        acc_t scur;  // summed scores of the tile about to be consumed
+        if (n_tiles > 0) {
+            wait_tile(0);
+            lds_exchange_barrier();
+            lds_byte* tb = stage_lds<T::TILE_BYTES, 0>();
+            acc_t sacc[2] = {(acc_t){}, (acc_t){}};
+#pragma unroll
+            for (int j = 0; j < T::KS; ++j) sacc[j & 1] = M::mma(k_frag(tb, j), qf[j], sacc[j & 1]);
+            scur = exchange(sacc[0] + sacc[1]);
+        }
+
+        // Weighted-sum MFMAs of the tile in stage tc with probabilities pb;
+        // mid() runs half way through (publishing the next tile's partial scores).
+        auto pv_phase = [&](lds_byte* tc, const bf16x8_t (&pb)[2], auto&& mid) {
+            constexpr int NPV = 2 * T::MBLK;
+            constexpr int PFV = 4;
+            bf16x8_t vring[PFV];
+#pragma unroll
+            for (int j = 0; j < PFV; ++j) vring[j] = v_frag(tc, j);
+#pragma unroll
+            for (int idx = 0; idx < NPV; ++idx) {
+                const int u = idx / T::MBLK, mb = idx % T::MBLK;
+                const bf16x8_t a = vring[idx % PFV];
+                if (idx + PFV < NPV) vring[idx % PFV] = v_frag(tc, idx + PFV);
+                o[mb] = M::mma(a, pb[u], o[mb]);
+                if (idx == 8) mid();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // ---- steady state: iteration i consumes tile i (PV) and scores tile i+1
+        auto iter = [&](auto SC, int i) {
+            constexpr int SI = decltype(SC)::value;              // stage of tile i
+            constexpr int SN = (SI + 1) % STAGES;                // stage of tile i+1
+            lds_byte* tc = stage_lds<T::TILE_BYTES, SI>();
+            lds_byte* tn = stage_lds<T::TILE_BYTES, SN>();
+            wait_tile(i + 1);
+            lds_exchange_barrier();  // tile i+1 visible to all waves
+            // Phase A: score MFMAs of tile i+1 interleaved with the softmax of tile i.
+            acc_t sacc[2] = {(acc_t){}, (acc_t){}};
+            bf16x8_t pb[2];
+            constexpr int PF = 4;
+            bf16x8_t kring[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) kring[j] = k_frag(tn, j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < T::KS; ++j) {
+                const bf16x8_t kf = kring[j % PF];
+                if (j + PF < T::KS) kring[j % PF] = k_frag(tn, j + PF);
+                sacc[j & 1] = M::mma(kf, qf[j], sacc[j & 1]);
+                if (j == 0) sm_max(scur, i);
+                if (j == 3) sm_rescale();
+                if (j == 5) sm_exp(scur, pb, 0);
+                if (j == 7) sm_exp(scur, pb, 4);
+                if (j == 9) sm_exp(scur, pb, 8);
+                if (j == 11) sm_exp(scur, pb, 12);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Phase B: weighted-sum MFMAs of tile i; partial scores of tile i+1
+            // go to the partner half way through.
+            acc_t part;
+            pv_phase(tc, pb, [&]() {
+                part = sacc[0] + sacc[1];
+                LDS_AS f32x4_t* mine = (LDS_AS f32x4_t*)(xbuf + wave * 4096);
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    mine[i4 * 64 + lane] = (f32x4_t){part[4 * i4], part[4 * i4 + 1], part[4 * i4 + 2], part[4 * i4 + 3]};
+            });
+            // Every wave is done with tile i and has published its partial
+            // scores of tile i+1: refill stage SI, then finish the exchange.
+            lds_exchange_barrier();
+            if (i + STAGES < n_tiles) issue_tile(IC<SI>{}, i + STAGES);
+            const LDS_AS f32x4_t* other = (const LDS_AS f32x4_t*)(xbuf + (wave ^ 1) * 4096);
+            f32x4_t ov[4];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) ov[i4] = other[i4 * 64 + lane];
+#pragma unroll
+            for (int i2 = 0; i2 < 16; ++i2) scur[i2] = part[i2] + ov[i2 >> 2][i2 & 3];
+        };
+        // Last tile: softmax and weighted sum only.  Every DMA has completed by
+        // now (the last wait was vmcnt(0)), so a runtime-selected stage is fine.
+        auto last_iter = [&](int i) {
+            const int st = i % STAGES;
+            lds_byte* tc = st == 0 ? stage_lds<T::TILE_BYTES, 0>()
+                         : st == 1 ? stage_lds<T::TILE_BYTES, 1>()
+                         : st == 2 ? stage_lds<T::TILE_BYTES, 2>()
+                                   : stage_lds<T::TILE_BYTES, (STAGES > 3 ? 3 : 0)>();
+            bf16x8_t pb[2];
+            sm_max(scur, i);
+            sm_rescale();
+            sm_exp(scur, pb, 0);
+            sm_exp(scur, pb, 4);
+            sm_exp(scur, pb, 8);
+            sm_exp(scur, pb, 12);
+            pv_phase(tc, pb, []() {});
+        };
+
+        const int n_full = n_tiles - 1;  // iterations that also score a next tile
+        for (int i0 = 0; i0 < n_full; i0 += STAGES) {
+            iter(IC<0>{}, i0);
+            if (i0 + 1 < n_full) iter(IC<1>{}, i0 + 1);
+            if (i0 + 2 < n_full) iter(IC<2>{}, i0 + 2);
+            if (STAGES > 3 && i0 + 3 < n_full) iter(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
+        }
+        if (n_tiles > 0) last_iter(n_full);
+
+        // ---- segment epilogue ----------------------------------------------
+        l_run += __shfl_xor(l_run, 32, 64);
+        if (head_ok) {
+            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            // accumulator entry i of block mb: column 256q + 32mb + (i/4)*8 + grp*4 + i%4
+            if (final_out) {
+                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc + 256 * q;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        bf16x4_t v;
+                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
+                    }
+                if (q == 0 && grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
+            } else {
+                float* prow = p.po + ((size_t)slot * p.h + head) * kDc + 256 * q;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4_t v;
+                        v[0] = o[mb][q4 * 4 + 0] * inv;
+                        v[1] = o[mb][q4 * 4 + 1] * inv;
+                        v[2] = o[mb][q4 * 4 + 2] * inv;
+                        v[3] = o[mb][q4 * 4 + 3] * inv;
+                        *(f32x4_t*)(prow + mb * 32 + q4 * 8 + grp * 4) = v;
+                    }
+                if (q == 0 && grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
+            }
+        }
+
+        pos = seg_end;
+        if (pos >= end) break;
+        wg_barrier();
+        ++r;
+        while (pv.cu()[r + 1] <= pos) ++r;
+    }
+}
+
+template <int P, int STAGES>
+hipError_t launch_pair_variant(const DecodeParams& p, hipStream_t stream)
+{
+    using T = PairTiling<P, STAGES>;
+    const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
+    decode_pair_kernel<P, STAGES><<<grid, T::THREADS, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
 template <int WH, int HS, int TS, int NT, int STAGES>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream)
 {
@@ -532,6 +998,11 @@ const VariantEntry kVariants[] = {
     {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>},
     {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>},
     {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>},
+    {64, 3, 32, &launch_pair_variant<2, 4>},
+    // The three-stage ring (pair kernel <2, 3>) is switched off: it took a GPU
+    // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
+    // cause has not been found; every other variant passes the same tests.
+    {32, 3, 32, &launch_pair_variant<1, 4>},
 };
 
 const VariantEntry* find_variant(int hpg, int variant)

@@ -74,10 +74,20 @@ BF16_CASES = [
     (64, {"heads_per_group": 64, "variant": 2}), (128, None),
     (128, {"heads_per_group": 128, "variant": 2}), (128, {"heads_per_group": 64}),
     (128, {"heads_per_group": 16}), (40, {"heads_per_group": 16}),
+    (64, {"heads_per_group": 64, "variant": 3}),
+    pytest.param(64, {"heads_per_group": 64, "variant": 4}, marks=pytest.mark.skip(
+        reason="three-stage pair kernel switched off after an unexplained GPU memory fault")),
+    (32, {"heads_per_group": 32, "variant": 3}),
+    (100, None), (16, {"heads_per_group": 16, "variant": 1}),
 ]
 
 
-@pytest.mark.parametrize("h,cfg", BF16_CASES, ids=[f"h{h}-{c}" for h, c in BF16_CASES])
+def _case_id(c):
+    h, cfg = c.values if hasattr(c, "values") else c
+    return f"h{h}-{cfg}"
+
+
+@pytest.mark.parametrize("h,cfg", BF16_CASES, ids=[_case_id(c) for c in BF16_CASES])
 def test_bf16_edges_every_output(mla, h, cfg):
     w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=100 + h, device="cuda")
     for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}):
