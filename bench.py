@@ -11,8 +11,10 @@ configuration gives no projection weights; the absorb inputs (q_nope, q_rope,
 W_UK, W_UV) are synthesized with the recipe of the end-to-end configuration.
 
 Timing: W untimed warm-up steps, then exactly K timed steps.  Before each
-timed step a 512 MiB buffer is overwritten (outside the timed events) so the
-latent cache cannot be served from the 4 MB L2s or the 256 MB Infinity Cache.
+timed step a 512 MiB buffer is read (outside the timed events) so the latent
+cache cannot be served from the 4 MB L2s or the 256 MB Infinity Cache; the
+eviction reads rather than writes so that no dirty lines are left whose
+write-back the timed step would pay for.
 HIP events on the library's stream bracket every step and, through the
 library's profiling hook, the split-KV attention kernel alone.  The whole
 timed loop is bracketed by torch.cuda.synchronize() on both sides.
@@ -39,7 +41,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 D_C, D_R, D_QK, D_K, D_V = 512, 64, 576, 128, 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", "decode_bf16.hip")
+# sources of the dominant (split-KV attention) kernel: the traffic figures in
+# TRAFFIC_FILE are only valid while these are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", f)
+               for f in ("decode_wide.hip", "bf16_common.h", "mla355_internal.h")]
 
 
 def log(*a):
@@ -85,8 +90,11 @@ class Hip:
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload):
@@ -147,10 +155,18 @@ def main():
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--hpg", type=int, default=0, help="heads per workgroup (0 = auto)")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (three times) and exit: "
+                         "the reference for scaling HBM traffic counters")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the hash of the attention kernel's sources and exit")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -160,6 +176,16 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
     cfg = workloads.CONFIGS[args.config]
     t_setup = time.perf_counter()
     w = workloads.make(args.config, device="cuda", poison=False)
@@ -177,7 +203,11 @@ def main():
     if args.variant:
         sched["variant"] = args.variant
     bufs = mla.alloc_step(w.b, w.h, w.t_max, w.dtype, config=sched or None)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Cache eviction between steps: READ a 512 MiB buffer (more than the 4 MB
+    # L2s plus the 256 MB Infinity Cache).  Reading leaves only clean lines
+    # behind; overwriting the buffer instead would leave ~256 MB of dirty lines
+    # whose write-back the next step would pay for.
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log("setup %.1f s: %s b=%d h=%d t_max=%d sum(L)=%d dtype=%s" %
         (time.perf_counter() - t_setup, cfg.name, w.b, w.h, w.t_max, sum(lens), w.dtype))
@@ -196,13 +226,13 @@ def main():
 
     for _ in range(W):
         if flush is not None:
-            flush.fill_(1)
+            flush.sum()
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush.sum()
         hip.record(ev[i][0], stream)
         step(i)
         hip.record(ev[i][3], stream)
@@ -260,7 +290,7 @@ def main():
         "step_flop": step_flop,
         "step_bytes": step_bytes,
         "ms_per_step_back_to_back": round(b2b_ms, 5),
-        "roofline": {"kernel": "split-KV attention (decode_bf16_kernel)",
+        "roofline": {"kernel": mla.mla_decode_kernel_name(w.dtype, w.h, sched or None),
                      "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(kms * 1e3, 2),

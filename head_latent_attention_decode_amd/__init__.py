@@ -59,13 +59,15 @@ _lib.mla_decode_workspace_bytes_ex.restype = _sz
 _lib.mla_decode_workspace_bytes_ex.argtypes = [_ci, _ci, _ci, _ci, ctypes.POINTER(MLAConfig)]
 _lib.mla_decode.restype = _ci
 _lib.mla_decode.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
+_lib.mla_decode_kernel_name.restype = ctypes.c_char_p
+_lib.mla_decode_kernel_name.argtypes = [_ci, _ci, ctypes.POINTER(MLAConfig)]
 _lib.mla_decode_ex.restype = _ci
 _lib.mla_decode_ex.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
                                ctypes.POINTER(MLAConfig), _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
-                    "mla_decode_ex")
+                    "mla_decode_ex", "mla_decode_kernel_name")
 
 
 class MLAError(RuntimeError):
@@ -129,6 +131,12 @@ def _cfg(config):
         else:
             setattr(c, k, int(v))
     return ctypes.pointer(c)
+
+
+def mla_decode_kernel_name(dtype: torch.dtype, h: int, config=None):
+    """Name of the attention kernel mla_decode would launch (pure host, no GPU); None if rejected."""
+    name = _lib.mla_decode_kernel_name(_dtype_code(dtype), h, _cfg(config))
+    return None if name is None else name.decode()
 
 
 def mla_decode_workspace_bytes(dtype: torch.dtype, b: int, h: int, t_max: int, config=None) -> int:

@@ -48,10 +48,12 @@ mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* c
         if (cfg && cfg->variant != 0) return MLA_ERR_UNSUPPORTED;
         s->min_chunk = 16;
     } else {
-        // <= 16 heads: single-wave 16-head workgroups (memory-bound regime);
-        // more heads: paired-wave 32x32-MFMA workgroups of 64 heads.
-        int hpg = h <= 16 ? 16 : h <= 32 ? 32 : 64;
-        int def_variant = h <= 16 ? 2 : h <= 32 ? 1 : 3;
+        // <= 16 heads: 16-head workgroups of two token-splitting waves
+        // (memory-bound regime); 17..64 heads: 32x32-MFMA workgroups of 32 or
+        // 64 heads; more: wide-wave workgroups covering 128 heads, so every
+        // latent row is fetched once per head group of 128.
+        int hpg = h <= 16 ? 16 : h <= 32 ? 32 : h <= 64 ? 64 : 128;
+        int def_variant = h <= 16 ? 1 : h <= 32 ? 1 : h <= 64 ? 3 : 4;
         if (cfg && cfg->heads_per_group != 0) {
             hpg = cfg->heads_per_group;
             def_variant = 1;
@@ -109,6 +111,15 @@ size_t mla_decode_workspace_bytes_ex(mla_dtype_t dt, int b, int h, int t_max,
     Schedule s;
     if (choose_schedule(dt, h, cfg, &s) != MLA_OK) return 0;
     return workspace_layout(b, h, s.n_chunks).total;
+}
+
+const char* mla_decode_kernel_name(mla_dtype_t dt, int h, const mla_decode_config_t* cfg)
+{
+    if (!dtype_ok(dt) || h <= 0) return nullptr;
+    Schedule s;
+    if (choose_schedule(dt, h, cfg, &s) != MLA_OK) return nullptr;
+    if (dt == MLA_DTYPE_F32) return "decode_f32_kernel";
+    return bf16_kernel_name(s.hpg, s.variant);
 }
 
 size_t mla_decode_workspace_bytes(mla_dtype_t dt, int b, int h, int t_max)

@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the bf16 decode kernels: vector
+// types, LDS-DMA wait and barrier helpers, per-stage LDS arrays, the MFMA
+// wrappers with their tile swizzles.  Everything sits in an anonymous
+// namespace, so each kernel file gets its own copies.
+#pragma once
+
+#include "mla355_internal.h"
+
+namespace mla355 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef LDS_AS unsigned char lds_byte;
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest tolerated growth
+constexpr float kNegBig = -1.0e30f;        // finite "minus infinity" for the running max
+// Buffer resource word 3 for raw (untyped, unswizzled) buffer access on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).  Issued
+// through the builtin so that the compiler's own wait insertion sees it.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+// Workgroup barrier ordering LDS only: the fences make every LDS access
+// before the barrier complete (lgkmcnt) and keep the compiler from moving LDS
+// accesses across it, without waiting for outstanding global loads.  Tile
+// data arrives by DMA, so its completion is awaited separately (vmcnt) by
+// the issuing wave before the barrier.
+__device__ __forceinline__ void wg_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier for data exchanged through ordinary LDS stores (not DMA): waits for
+// this wave's LDS accesses (lgkmcnt) only.  A release fence on LDS would also
+// wait for every DMA still landing in other stages (the compiler counts those
+// as LDS writes), which would serialise the tile prefetch with compute.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_exchange_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One LDS array per pipeline stage.  Distinct objects let the compiler prove
+// that reads of one stage do not alias DMA still landing in another, so it
+// does not insert conservative vmcnt(0) waits before them.
+template <int BYTES, int S>
+__device__ __forceinline__ lds_byte* stage_lds()
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[BYTES];
+    return (lds_byte*)buf;
+}
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int WH>
+struct Mfma;
+
+template <>
+struct Mfma<16> {
+    typedef f32x4_t acc_t;
+    static constexpr int kK = 32;      // contraction per instruction
+    static constexpr int kAcc = 4;     // fp32 accumulators per lane
+    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Region-A swizzle (4 bits): rows 0..15 all distinct (b128 reads of 16
+    // rows), and rows 0..7 / 8..15 land in distinct 32-byte pairs (b64
+    // transposed reads of a 16-column strip by 8 rows).
+    __device__ __forceinline__ static int xa(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+};
+
+template <>
+struct Mfma<32> {
+    typedef f32x16_t acc_t;
+    static constexpr int kK = 16;
+    static constexpr int kAcc = 16;
+    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // rows 0..15 distinct, and each run of 4 rows lands in distinct 64-byte
+    // quads (b64 transposed reads of a 32-column strip by 4 rows).
+    __device__ __forceinline__ static int xa(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+
+// Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.
+__device__ __forceinline__ int xb(int r) { return (r >> 1) & 7; }
+
+}  // namespace
+}  // namespace mla355

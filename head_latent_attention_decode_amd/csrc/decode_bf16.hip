@@ -34,115 +34,13 @@
 //    merge their (m, l, O) through LDS at the end of a segment.
 //  * Segment end: a row finished inside this chunk writes out (bf16) and lse;
 //    otherwise the normalised fp32 partial and its lse go to the row's slot.
-#include "mla355_internal.h"
+#include "bf16_common.h"
 
 #include <math.h>
 
 namespace mla355 {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-#define LDS_AS __attribute__((address_space(3)))
-typedef LDS_AS unsigned char lds_byte;
-
-constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest tolerated growth
-constexpr float kNegBig = -1.0e30f;        // finite "minus infinity" for the running max
-// Buffer resource word 3 for raw (untyped, unswizzled) buffer access on gfx9-family parts.
-constexpr int kBufferFlags = 0x00020000;
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima).  Issued
-// through the builtin so that the compiler's own wait insertion sees it.
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
-}
-
-// Workgroup barrier ordering LDS only: the fences make every LDS access
-// before the barrier complete (lgkmcnt) and keep the compiler from moving LDS
-// accesses across it, without waiting for outstanding global loads.  Tile
-// data arrives by DMA, so its completion is awaited separately (vmcnt) by
-// the issuing wave before the barrier.
-__device__ __forceinline__ void wg_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Barrier for data exchanged through ordinary LDS stores (not DMA): waits for
-// this wave's LDS accesses (lgkmcnt) only.  A release fence on LDS would also
-// wait for every DMA still landing in other stages (the compiler counts those
-// as LDS writes), which would serialise the tile prefetch with compute.  The
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_exchange_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// One LDS array per pipeline stage.  Distinct objects let the compiler prove
-// that reads of one stage do not alias DMA still landing in another, so it
-// does not insert conservative vmcnt(0) waits before them.
-template <int BYTES, int S>
-__device__ __forceinline__ lds_byte* stage_lds()
-{
-    __shared__ __attribute__((aligned(1024))) unsigned char buf[BYTES];
-    return (lds_byte*)buf;
-}
-
-template <int V>
-struct IC {
-    static constexpr int value = V;
-};
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int WH>
-struct Mfma;
-
-template <>
-struct Mfma<16> {
-    typedef f32x4_t acc_t;
-    static constexpr int kK = 32;      // contraction per instruction
-    static constexpr int kAcc = 4;     // fp32 accumulators per lane
-    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    // Region-A swizzle (4 bits): rows 0..15 all distinct (b128 reads of 16
-    // rows), and rows 0..7 / 8..15 land in distinct 32-byte pairs (b64
-    // transposed reads of a 16-column strip by 8 rows).
-    __device__ __forceinline__ static int xa(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-};
-
-template <>
-struct Mfma<32> {
-    typedef f32x16_t acc_t;
-    static constexpr int kK = 16;
-    static constexpr int kAcc = 16;
-    __device__ __forceinline__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    // rows 0..15 distinct, and each run of 4 rows lands in distinct 64-byte
-    // quads (b64 transposed reads of a 32-column strip by 4 rows).
-    __device__ __forceinline__ static int xa(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-};
-
-// Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.
-__device__ __forceinline__ int xb(int r) { return (r >> 1) & 7; }
 
 template <int WH, int HS, int TS, int NT, int STAGES>
 struct Tiling {
@@ -986,23 +884,29 @@ struct VariantEntry {
     int variant;
     int tile_tokens;
     hipError_t (*launch)(const DecodeParams&, hipStream_t);
+    const char* name;   // kernel name as profilers print it
 };
 
 // heads_per_group, variant id, tile tokens, launcher <WH, HS, TS, NT, STAGES>
 const VariantEntry kVariants[] = {
-    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>},
-    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>},
-    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>},
-    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>},
-    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>},
-    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>},
-    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>},
-    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>},
-    {64, 3, 32, &launch_pair_variant<2, 4>},
+    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2>"},
+    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>, "decode_bf16_kernel<16, 1, 1, 32, 2>"},
+    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>, "decode_bf16_kernel<16, 2, 2, 32, 2>"},
+    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>, "decode_bf16_kernel<32, 1, 1, 32, 2>"},
+    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>, "decode_bf16_kernel<16, 4, 1, 64, 2>"},
+    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>, "decode_bf16_kernel<32, 2, 1, 32, 4>"},
+    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>, "decode_bf16_kernel<32, 4, 1, 32, 4>"},
+    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>, "decode_bf16_kernel<16, 8, 1, 32, 2>"},
+    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>"},
     // The three-stage ring (pair kernel <2, 3>) is switched off: it took a GPU
     // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
     // cause has not been found; every other variant passes the same tests.
-    {32, 3, 32, &launch_pair_variant<1, 4>},
+    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>"},
+    {128, 3, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4>"},
+    {128, 4, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3>"},
+    {64, 5, 32, &launch_decode_wide<2, 4>, "decode_wide_kernel<2, 4>"},
+    {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2>"},
+    {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3>"},
 };
 
 const VariantEntry* find_variant(int hpg, int variant)
@@ -1018,6 +922,12 @@ const VariantEntry* find_variant(int hpg, int variant)
 bool bf16_variant_exists(int heads_per_group, int variant)
 {
     return find_variant(heads_per_group, variant) != nullptr;
+}
+
+const char* bf16_kernel_name(int heads_per_group, int variant)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    return v ? v->name : nullptr;
 }
 
 int bf16_tile_tokens(int heads_per_group, int variant)

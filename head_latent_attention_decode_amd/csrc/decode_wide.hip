@@ -1,0 +1,375 @@
+// Split-KV absorbed-MLA decode, bf16 in / fp32 accumulate: the wide-wave
+// kernel for 32 or more heads.
+//
+// Same operation, plan and partial format as the other bf16 kernels (the
+// glossary page "Multi-head Latent Attention", section on why decode absorbs
+// the matrices: absorbed query heads score directly against the shared latent
+// rows, and the softmax-weighted sum of the c_KV parts is the output).
+//
+// Layout of the work:
+//  * One workgroup = NW waves = one token chunk x 32*NW heads.  Every wave owns
+//    32 heads outright: their 576-wide queries stay in VGPRs for the whole
+//    chunk (the B operand of every score MFMA) and their 512-wide fp32 output
+//    accumulators stay in AGPRs.  No wave needs anything from another except
+//    the shared latent tile, so one barrier per tile is the only
+//    synchronisation.
+//  * With 128 heads a single workgroup covers every head, so each latent row
+//    is fetched from HBM exactly once.
+//  * Tiles of 32 latent rows stream HBM -> LDS with direct-to-LDS 16-byte DMA
+//    (STAGES-deep ring, STAGES-1 tiles in flight), laid out as in the other
+//    kernels: region A = first 1024 B of each row (one DMA instruction per
+//    row), region B = last 128 B (8 rows per instruction), 16-byte chunks
+//    XOR-swizzled per row.  The refill DMA of a tile is spread over the first
+//    score MFMAs rather than issued as one burst.
+//  * Per tile and wave (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//      S^T[32 tok x 32 heads] = K . Q'^T   36 MFMAs, A = latent rows read from
+//                                          LDS (ds_read_b128), B = queries;
+//      online softmax on S^T (each lane holds one head: lane-local running
+//      max/sum, one cross-lane step for the tile max);
+//      O^T[512 x 32 heads] += V^T . P^T    32 MFMAs, A = latent rows read
+//                                          transposed (ds_read_b64_tr_b16),
+//                                          B = P^T straight from the S^T
+//                                          accumulator layout.
+//  * Online softmax in base 2, lazy rescale (only when the running max grows
+//    by more than 2^8), exact final normalisation.
+#include "bf16_common.h"
+
+#include <math.h>
+
+namespace mla355 {
+namespace {
+
+template <int NW, int STAGES>
+struct WideTiling {
+    static constexpr int THREADS = NW * 64;
+    static constexpr int HG = 32 * NW;                 // heads per workgroup
+    static constexpr int N = 32;                       // tokens per tile
+    static constexpr int A_BYTES = N * 1024;
+    static constexpr int TILE_BYTES = N * kRowBytesBf16;
+    static constexpr int LOADS_A = N / NW;             // region-A DMA instructions per wave
+    static constexpr int GROUPS_B = N / 8;             // region-B DMA instructions per tile
+    static constexpr int LOADS_B = GROUPS_B / NW > 0 ? GROUPS_B / NW : 1;
+    static constexpr int LOADS = LOADS_A + LOADS_B;    // DMA instructions per wave per tile
+    static constexpr int KS = kDqk / 16;               // 36 score k-steps
+    static constexpr int KSA = kDc / 16;               // 32 of them in region A
+    static constexpr int MBLK = kDc / 32;              // 16 output blocks of 32 columns
+    static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
+    static_assert(GROUPS_B % NW == 0, "region-B groups split evenly over waves");
+    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+    static_assert(STAGES * TILE_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((STAGES - 2) * LOADS <= 63, "vmcnt range");
+    static_assert(LOADS <= KS, "DMA spread over the score steps");
+};
+
+template <int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
+{
+    using T = WideTiling<NW, STAGES>;
+    using M = Mfma<32>;
+    typedef f32x16_t acc_t;
+
+    const int lane = threadIdx.x & 63;
+    // wave index is uniform: keep it (and all DMA arithmetic built on it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane & 31;    // head inside the wave's 32
+    const int grp = lane >> 5;   // k-slot group (0/1) of the MFMA operand layouts
+
+    // Workgroup -> (chunk k, head group hg).  Blocks go round-robin to the 8
+    // XCDs (block i -> XCD i % 8); all head groups of a chunk share an XCD so
+    // they share its L2 copy of the chunk's tiles.
+    int k, hg;
+    if (p.n_hg == 1) {
+        k = blockIdx.x;
+        hg = 0;
+    } else {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        k = (slot / p.n_hg) * 8 + xcd;
+        hg = slot % p.n_hg;
+    }
+    const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
+    const int total = p.plan[0];
+    const int chunk = p.plan[1];
+    int r = pv.chunk_row()[k];
+    if (r < 0) return;
+    int pos = k * chunk;
+    const int end = pos + min(chunk, total - pos);
+
+    const __bf16* __restrict__ qg = (const __bf16*)p.q;
+    const unsigned char* __restrict__ cg = (const unsigned char*)p.cache;
+    const int head = hg * T::HG + wave * 32 + hl;
+    const bool head_ok = head < p.h;
+    const float c2 = p.scale_log2;
+
+    // ---- per-lane LDS offsets --------------------------------------------
+    // Score step j reads token row rr = lane & 31, 8 channels starting at
+    // 16j + 8grp: logical 16-byte chunk 2j + grp of region A (j < 32), or
+    // chunk 2(j-32) + grp of region B.
+    const int rr = lane & 31;
+    int koffA[8], koffB[4];
+    {
+        const int x = M::xa(rr & 15);
+        const int xbv = xb(rr & 15);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) koffA[j] = rr * 1024 + (((2 * j + grp) ^ x) << 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) koffB[j] = T::A_BYTES + rr * 128 + (((2 * j + grp) ^ xbv) << 4);
+    }
+    // Transposed reads of 16 tokens x 32 columns: this lane supplies 4
+    // columns of token row0 (+8); the instruction hands every lane one column
+    // and 4 tokens.  Columns 32mb + 16((lane>>4)&1) + 4(lane&3) .. +3.
+    int voff0[4], voff1[4];
+    {
+        const int row0 = grp * 4 + ((lane & 15) >> 2);
+        const int x0 = M::xa(row0 & 15), x1 = M::xa((row0 + 8) & 15);
+        const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            voff0[j] = row0 * 1024 + (((4 * j + cc) ^ x0) << 4) + ((lane & 1) << 3);
+            voff1[j] = (row0 + 8) * 1024 + (((4 * j + cc) ^ x1) << 4) + ((lane & 1) << 3);
+        }
+    }
+
+    while (true) {
+        const int row_lo = pv.cu()[r];
+        const int row_hi = pv.cu()[r + 1];
+        const int seg_end = min(end, row_hi);
+        const int seg_a = pos - row_lo;
+        const int seg_len = seg_end - pos;
+        const int split_j = k - row_lo / chunk;
+        const bool final_out = pv.nsplit()[r] == 1;
+        const int slot = pv.base()[r] + split_j;
+        const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
+        const int n_tiles = (seg_len + T::N - 1) / T::N;
+
+        // Queries (B operand): lane -> head hl, channels 16j + 8grp .. +7 of step j.
+        bf16x8_t qf[T::KS];
+        {
+            const bf16x8_t* qrow =
+                (const bf16x8_t*)(qg + ((size_t)r * p.h + (head_ok ? head : 0)) * kDqk);
+#pragma unroll
+            for (int j = 0; j < T::KS; ++j) {
+                bf16x8_t v = qrow[2 * j + grp];
+                if (!head_ok) v = (bf16x8_t){};
+                qf[j] = v;
+            }
+        }
+
+        // DMA instruction `li` (0 .. LOADS-1) of this wave's share of `tile`
+        // into stage SC.  Rows past the segment end re-read its last row (the
+        // scores of those slots are masked), so every access stays inside the
+        // rows of this segment.
+        auto issue_load = [&](auto SC, int tile, int li) {
+            const int t0 = tile * T::N;
+            const int last = min(T::N, seg_len - t0) - 1;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(seg_base + (size_t)t0 * kRowBytesBf16), (short)0,
+                (last + 1) * kRowBytesBf16, kBufferFlags);
+            lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
+            if (li < T::LOADS_A) {
+                const int row = wave + li * NW;
+                const int srow = min(row, last);
+                const unsigned voff = (unsigned)((lane ^ M::xa(row & 15)) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (LDS_AS void*)(st + row * 1024), 16, voff,
+                    __builtin_amdgcn_readfirstlane(srow * kRowBytesBf16), 0, 0);
+            } else {
+                const int gb = wave + (li - T::LOADS_A) * NW;
+                const int row = gb * 8 + (lane >> 3);
+                const int srow = min(row, last);
+                const int lc = (lane & 7) ^ xb(row & 15);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (LDS_AS void*)(st + T::A_BYTES + gb * 1024), 16,
+                    (unsigned)(srow * kRowBytesBf16 + 1024 + lc * 16), 0, 0, 0);
+            }
+        };
+        auto issue_tile = [&](auto SC, int tile) {
+#pragma unroll
+            for (int li = 0; li < T::LOADS; ++li) issue_load(SC, tile, li);
+        };
+        // Wait until this wave's share of tile t has landed: the tiles issued
+        // after it are t+1 .. min(t+STAGES-2, n_tiles-1).
+        auto wait_tile = [&](int t) {
+            const int after = min(STAGES - 2, n_tiles - 1 - t);
+            if (STAGES > 3 && after >= 2)
+                wait_vmcnt<(STAGES > 3 ? 2 : 0) * T::LOADS>();
+            else if (STAGES > 2 && after >= 1)
+                wait_vmcnt<(STAGES > 2 ? 1 : 0) * T::LOADS>();
+            else
+                wait_vmcnt<0>();
+        };
+
+        acc_t o[T::MBLK];
+#pragma unroll
+        for (int mb = 0; mb < T::MBLK; ++mb) o[mb] = (acc_t){};
+        float m_run = kNegBig;
+        float l_run = 0.f;
+
+        auto k_frag = [&](lds_byte* tb, int j) -> bf16x8_t {
+            const lds_byte* a = (j < T::KSA) ? tb + koffA[j % 8] + (j / 8) * 256 : tb + koffB[j - T::KSA];
+            return *(const LDS_AS bf16x8_t*)a;
+        };
+        // Transposed V fragment idx: token half u = idx / MBLK, column block mb = idx % MBLK.
+        auto v_frag = [&](lds_byte* tb, int idx) -> bf16x8_t {
+            const int u = idx / T::MBLK, mb = idx % T::MBLK;
+            const int blk = (mb / 4) * 256 + u * 16 * 1024;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff0[mb % 4] + blk));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff1[mb % 4] + blk));
+            return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+        };
+
+        // One tile: tile index i in stage SC.
+        auto step = [&](auto SC, int i) {
+            constexpr int S = decltype(SC)::value;
+            constexpr int SR = (S + STAGES - 1) % STAGES;  // stage of tile i-1 = refill target
+            lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
+            wait_tile(i);
+            lds_exchange_barrier();  // tile i visible to all; everyone is done with tile i-1
+            const bool refill = i + STAGES - 1 < n_tiles;
+
+            // ---- scores: S^T = K . Q'^T, refill DMA spread over the first steps
+            acc_t sacc = (acc_t){};
+            constexpr int PF = 4;
+            bf16x8_t kring[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) kring[j] = k_frag(tb, j);
+#pragma unroll
+            for (int j = 0; j < T::KS; ++j) {
+                const bf16x8_t kf = kring[j % PF];
+                if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
+                sacc = M::mma(kf, qf[j], sacc);
+                if (j < T::LOADS && refill) issue_load(IC<SR>{}, i + STAGES - 1, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
+            const int tvalid = __builtin_amdgcn_readfirstlane(seg_len - i * T::N);
+            if (tvalid < T::N) {
+                const int lim = tvalid - 4 * grp;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if ((e >> 2) * 8 + (e & 3) >= lim) sacc[e] = -INFINITY;
+            }
+            float tm = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+            for (int e = 3; e < 16; ++e) tm = fmaxf(tm, sacc[e]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, tm),
+                                                             __builtin_bit_cast(unsigned, tm), false, false);
+            const float tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
+            const float m_new = fmaxf(m_run, tmax);
+            if (__any(m_new > m_run + kRescaleThreshold)) {
+                const float alpha = exp2_fast(m_run - m_new);
+                l_run *= alpha;
+                // The accumulators live in AGPRs; the empty asm statements pin
+                // the copy used for the multiply to VGPRs and the result back
+                // to AGPRs, one block at a time (left to itself the register
+                // allocator moves all 256 accumulators and spills).
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb) {
+                    acc_t t = o[mb];
+                    asm volatile("" : "+v"(t));
+                    t *= alpha;
+                    asm volatile("" : "+a"(t));
+                    o[mb] = t;
+                }
+                m_run = m_new;
+            }
+            bf16x8_t pb[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float x = exp2_fast(__builtin_fmaf(sacc[e], c2, -m_run));
+                l_run += x;
+                pb[e >> 3][e & 7] = (__bf16)x;
+            }
+
+            // ---- weighted sum: O^T += V^T . P^T
+            constexpr int NPV = 2 * T::MBLK;
+            constexpr int PFV = 4;
+            bf16x8_t vring[PFV];
+#pragma unroll
+            for (int j = 0; j < PFV; ++j) vring[j] = v_frag(tb, j);
+#pragma unroll
+            for (int idx = 0; idx < NPV; ++idx) {
+                const int u = idx / T::MBLK, mb = idx % T::MBLK;
+                const bf16x8_t a = vring[idx % PFV];
+                if (idx + PFV < NPV) vring[idx % PFV] = v_frag(tb, idx + PFV);
+                o[mb] = M::mma(a, pb[u], o[mb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // ---- prologue: tiles 0 .. STAGES-2 in flight ------------------------
+        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
+        if (STAGES > 2 && 1 < n_tiles) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
+        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
+        for (int i0 = 0; i0 < n_tiles; i0 += STAGES) {
+            step(IC<0>{}, i0);
+            if (i0 + 1 < n_tiles) step(IC<1 % STAGES>{}, i0 + 1);
+            if (STAGES > 2 && i0 + 2 < n_tiles) step(IC<(STAGES > 2 ? 2 : 0)>{}, i0 + 2);
+            if (STAGES > 3 && i0 + 3 < n_tiles) step(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
+        }
+
+        // ---- segment epilogue ----------------------------------------------
+        l_run += __shfl_xor(l_run, 32, 64);
+        if (head_ok) {
+            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
+            if (final_out) {
+                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        bf16x4_t v;
+                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
+                    }
+                if (grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
+            } else {
+                float* prow = p.po + ((size_t)slot * p.h + head) * kDc;
+#pragma unroll
+                for (int mb = 0; mb < T::MBLK; ++mb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4_t v;
+                        v[0] = o[mb][q4 * 4 + 0] * inv;
+                        v[1] = o[mb][q4 * 4 + 1] * inv;
+                        v[2] = o[mb][q4 * 4 + 2] * inv;
+                        v[3] = o[mb][q4 * 4 + 3] * inv;
+                        *(f32x4_t*)(prow + mb * 32 + q4 * 8 + grp * 4) = v;
+                    }
+                if (grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
+            }
+        }
+
+        pos = seg_end;
+        if (pos >= end) break;
+        wg_barrier();  // every wave is done with the stages before they are refilled
+        ++r;
+        while (pv.cu()[r + 1] <= pos) ++r;
+    }
+}
+
+}  // namespace
+
+template <int NW, int STAGES>
+hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream)
+{
+    using T = WideTiling<NW, STAGES>;
+    const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
+    decode_wide_kernel<NW, STAGES><<<grid, T::THREADS, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template hipError_t launch_decode_wide<4, 4>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<4, 3>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<2, 4>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<2, 2>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<1, 3>(const DecodeParams&, hipStream_t);
+
+}  // namespace mla355

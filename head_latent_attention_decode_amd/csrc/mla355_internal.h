@@ -92,8 +92,13 @@ struct Bf16Variant {
 };
 bool bf16_variant_exists(int heads_per_group, int variant);
 int bf16_tile_tokens(int heads_per_group, int variant);
+const char* bf16_kernel_name(int heads_per_group, int variant);
 hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
                               hipStream_t stream);
+
+// Wide-wave bf16 kernel: NW waves of 32 heads each, STAGES-deep LDS ring.
+template <int NW, int STAGES>
+hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
 

@@ -142,6 +142,16 @@ mla_status_t mla_decode_ex(mla_dtype_t dtype, int b, int h, int t_max, const voi
                            const mla_decode_config_t* config, void* stream);
 
 /*
+ * mla_decode_kernel_name -- name of the split-KV attention kernel that
+ * mla_decode_ex would launch for this dtype, head count and config (config
+ * may be NULL: automatic), as profilers list it (for example
+ * "decode_wide_kernel<4, 3>").  Pure host function: no HIP call, no GPU
+ * needed.  The string is static and owned by the library.  Returns NULL for
+ * an unknown dtype, h <= 0 or a config mla_decode_ex would reject.
+ */
+const char* mla_decode_kernel_name(mla_dtype_t dtype, int h, const mla_decode_config_t* config);
+
+/*
  * mla_absorb_o -- output absorption.
  *   y[b,h,:] = o[b,h,:] . W_UV[h]   (contracts d_c = 512)
  * Glossary, section on why decode absorbs: sum_t p_t (c_t W^UV_h) equals

@@ -118,3 +118,16 @@ def test_python_binding_checks_tensors(mla):
                        torch.zeros(2, dtype=torch.int32), 0.07)
     with pytest.raises(TypeError):
         mla.mla_decode_workspace_bytes(torch.float16, 2, 16, 8)
+
+
+def test_decode_kernel_name_host_only(mla):
+    # the schedule picks a kernel per head count; the query makes no HIP call
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 128) == "decode_wide_kernel<4, 3>"
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 16).startswith("decode_bf16_kernel<16,")
+    assert mla.mla_decode_kernel_name(torch.float32, 16) == "decode_f32_kernel"
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"heads_per_group": 64, "variant": 3}) == \
+        "decode_pair_kernel<2, 4>"
+    # rejected configurations give no name
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 0) is None
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"heads_per_group": 64, "variant": 4}) is None
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"variant": 99}) is None
