@@ -110,7 +110,7 @@ size_t mla_decode_workspace_bytes_ex(mla_dtype_t dt, int b, int h, int t_max,
     if (!dtype_ok(dt) || !dims_ok(b, h, t_max)) return 0;
     Schedule s;
     if (choose_schedule(dt, h, cfg, &s) != MLA_OK) return 0;
-    return workspace_layout(b, h, s.n_chunks).total;
+    return workspace_layout(b, h, s.n_chunks, dt == MLA_DTYPE_BF16 ? 2 : 4).total;
 }
 
 const char* mla_decode_kernel_name(mla_dtype_t dt, int h, const mla_decode_config_t* cfg)
@@ -141,7 +141,7 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     Schedule s;
     const mla_status_t st = choose_schedule(dt, h, cfg, &s);
     if (st != MLA_OK) return st;
-    const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks);
+    const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks, dt == MLA_DTYPE_BF16 ? 2 : 4);
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t hs = (hipStream_t)stream;
@@ -154,7 +154,7 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     p.out = out;
     p.lse = lse;
     p.plse = (float*)(ws + w.plse_off);
-    p.po = (float*)(ws + w.po_off);
+    p.po = (void*)(ws + w.po_off);
     p.b = b;
     p.h = h;
     p.t_max = t_max;

@@ -60,6 +60,15 @@ __device__ __forceinline__ void lds_exchange_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Orders this wave's own LDS traffic: its earlier LDS accesses complete
+// before its later ones issue (for data a wave stages through LDS for itself).
+__device__ __forceinline__ void lds_wave_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
 // One LDS array per pipeline stage.  Distinct objects let the compiler prove
 // that reads of one stage do not alias DMA still landing in another, so it
 // does not insert conservative vmcnt(0) waits before them.
@@ -108,6 +117,20 @@ struct Mfma<32> {
     // quads (b64 transposed reads of a 32-column strip by 4 rows).
     __device__ __forceinline__ static int xa(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 };
+
+// Workgroup -> (chunk k, head group hg).  Workgroups are dispatched
+// round-robin over the 8 XCDs (block i -> XCD i % 8), each with its own L2.
+// XCD x takes a contiguous run of n_chunks / 8 chunks with all their head
+// groups: the head groups of a chunk share that L2's copy of its latent tiles,
+// and the consecutive chunks of one batch row share its query rows.
+// n_chunks is a multiple of 8.
+__device__ __forceinline__ void block_work(int n_chunks, int n_hg, int& k, int& hg)
+{
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    k = xcd * (n_chunks >> 3) + slot / n_hg;
+    hg = slot % n_hg;
+}
 
 // Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.
 __device__ __forceinline__ int xb(int r) { return (r >> 1) & 7; }

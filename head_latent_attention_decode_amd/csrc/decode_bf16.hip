@@ -83,19 +83,8 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
     const int hl = lane & (WH - 1);   // this lane's head inside the wave's WH heads
     const int grp = lane / WH;        // lane group sharing that head (0..64/WH-1)
 
-    // Workgroup -> (chunk k, head group hg).  Dispatch is round-robin over the
-    // 8 XCDs (block i -> XCD i % 8); all head groups of one chunk get the same
-    // XCD so they share its L2 copy of the chunk's tiles.
     int k, hg;
-    if (p.n_hg == 1) {
-        k = blockIdx.x;
-        hg = 0;
-    } else {
-        const int xcd = blockIdx.x & 7;
-        const int slot = blockIdx.x >> 3;
-        k = (slot / p.n_hg) * 8 + xcd;
-        hg = slot % p.n_hg;
-    }
+    block_work(p.n_chunks, p.n_hg, k, hg);
     const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
     const int total = p.plan[0];
     const int chunk = p.plan[1];
@@ -399,37 +388,23 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
             // O^T accumulator entry i of block mb is latent column
             //   WH=16: mb*16 + grp*4 + i       WH=32: mb*32 + (i/4)*8 + grp*4 + i%4
-            if (final_out) {
-                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc;
+            // a row finished here writes out/lse; otherwise its slot's partial
+            // (normalised, in the input dtype) and partial lse
+            __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
+                                      : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head * kDc;
 #pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
+            for (int mb = 0; mb < T::MBLK; ++mb)
 #pragma unroll
-                    for (int q4 = 0; q4 < M::kAcc / 4; ++q4) {
-                        const int c = mb * WH + q4 * 8 + grp * 4;
-                        bf16x4_t v;
-                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
-                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
-                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
-                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
-                        *(bf16x4_t*)(orow + c) = v;
-                    }
-                if (grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
-            } else {
-                float* prow = p.po + ((size_t)slot * p.h + head) * kDc;
-#pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
-#pragma unroll
-                    for (int q4 = 0; q4 < M::kAcc / 4; ++q4) {
-                        const int c = mb * WH + q4 * 8 + grp * 4;
-                        f32x4_t v;
-                        v[0] = o[mb][q4 * 4 + 0] * inv;
-                        v[1] = o[mb][q4 * 4 + 1] * inv;
-                        v[2] = o[mb][q4 * 4 + 2] * inv;
-                        v[3] = o[mb][q4 * 4 + 3] * inv;
-                        *(f32x4_t*)(prow + c) = v;
-                    }
-                if (grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
-            }
+                for (int q4 = 0; q4 < M::kAcc / 4; ++q4) {
+                    const int c = mb * WH + q4 * 8 + grp * 4;
+                    bf16x4_t v;
+                    v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                    v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                    v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                    v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                    *(bf16x4_t*)(orow + c) = v;
+                }
+            if (grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head] = lse_v;
         }
 
         pos = seg_end;
@@ -505,15 +480,7 @@ __global__ __launch_bounds__(P * 128) void decode_pair_kernel(DecodeParams p)
     const int grp = lane >> 5;         // k-slot group (0/1)
 
     int k, hg;
-    if (p.n_hg == 1) {
-        k = blockIdx.x;
-        hg = 0;
-    } else {
-        const int xcd = blockIdx.x & 7;
-        const int slot = blockIdx.x >> 3;
-        k = (slot / p.n_hg) * 8 + xcd;
-        hg = slot % p.n_hg;
-    }
+    block_work(p.n_chunks, p.n_hg, k, hg);
     const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
     const int total = p.plan[0];
     const int chunk = p.plan[1];
@@ -822,35 +789,20 @@ __global__ __launch_bounds__(P * 128) void decode_pair_kernel(DecodeParams p)
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
             const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
             // accumulator entry i of block mb: column 256q + 32mb + (i/4)*8 + grp*4 + i%4
-            if (final_out) {
-                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc + 256 * q;
+            __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
+                                      : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head * kDc + 256 * q;
 #pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
+            for (int mb = 0; mb < T::MBLK; ++mb)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        bf16x4_t v;
-                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
-                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
-                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
-                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
-                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
-                    }
-                if (q == 0 && grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
-            } else {
-                float* prow = p.po + ((size_t)slot * p.h + head) * kDc + 256 * q;
-#pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        f32x4_t v;
-                        v[0] = o[mb][q4 * 4 + 0] * inv;
-                        v[1] = o[mb][q4 * 4 + 1] * inv;
-                        v[2] = o[mb][q4 * 4 + 2] * inv;
-                        v[3] = o[mb][q4 * 4 + 3] * inv;
-                        *(f32x4_t*)(prow + mb * 32 + q4 * 8 + grp * 4) = v;
-                    }
-                if (q == 0 && grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
-            }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    bf16x4_t v;
+                    v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                    v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                    v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                    v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                    *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
+                }
+            if (q == 0 && grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head] = lse_v;
         }
 
         pos = seg_end;
@@ -902,9 +854,9 @@ const VariantEntry kVariants[] = {
     // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
     // cause has not been found; every other variant passes the same tests.
     {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>"},
-    {128, 3, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4>"},
-    {128, 4, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3>"},
-    {64, 5, 32, &launch_decode_wide<2, 4>, "decode_wide_kernel<2, 4>"},
+    {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3>"},
+    {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2>"},
+    {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3>"},
     {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2>"},
     {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3>"},
 };

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p)
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
             const float lse_v = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
             float* dst = final_out ? (float*)p.out + ((size_t)r * p.h + head) * kDc
-                                   : p.po + ((size_t)slot * p.h + head) * kDc;
+                                   : (float*)p.po + ((size_t)slot * p.h + head) * kDc;
 #pragma unroll
             for (int j = 0; j < kDc / kTok; ++j) dst[tt + kTok * j] = acc[j] * inv;
             if (tt == 0) {

@@ -16,11 +16,12 @@
 //  * With 128 heads a single workgroup covers every head, so each latent row
 //    is fetched from HBM exactly once.
 //  * Tiles of 32 latent rows stream HBM -> LDS with direct-to-LDS 16-byte DMA
-//    (STAGES-deep ring, STAGES-1 tiles in flight), laid out as in the other
-//    kernels: region A = first 1024 B of each row (one DMA instruction per
-//    row), region B = last 128 B (8 rows per instruction), 16-byte chunks
-//    XOR-swizzled per row.  The refill DMA of a tile is spread over the first
-//    score MFMAs rather than issued as one burst.
+//    (STAGES-deep ring, STAGES-1 tiles in flight).  A tile is stored as
+//    region A = the first 1024 B of each row (one DMA instruction per row,
+//    rows padded to 1280 B) and region B = the last 128 B (8 rows per
+//    instruction); see the per-lane offsets below for the swizzles.  The
+//    refill DMA of a tile is spread over the first score MFMAs rather than
+//    issued as one burst.
 //  * Per tile and wave (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //      S^T[32 tok x 32 heads] = K . Q'^T   36 MFMAs, A = latent rows read from
 //                                          LDS (ds_read_b128), B = queries;
@@ -39,13 +40,17 @@
 namespace mla355 {
 namespace {
 
+// Chunk rotation of region-A row r (see the per-lane offsets in the kernel).
+__device__ __forceinline__ int rot16(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
 template <int NW, int STAGES>
 struct WideTiling {
     static constexpr int THREADS = NW * 64;
     static constexpr int HG = 32 * NW;                 // heads per workgroup
     static constexpr int N = 32;                       // tokens per tile
-    static constexpr int A_BYTES = N * 1024;
-    static constexpr int TILE_BYTES = N * kRowBytesBf16;
+    static constexpr int ROW_A = 1024 + 256;              // LDS stride of a region-A row (rotated)
+    static constexpr int A_BYTES = N * ROW_A;
+    static constexpr int TILE_BYTES = A_BYTES + N * 128;  // + region B
     static constexpr int LOADS_A = N / NW;             // region-A DMA instructions per wave
     static constexpr int GROUPS_B = N / 8;             // region-B DMA instructions per tile
     static constexpr int LOADS_B = GROUPS_B / NW > 0 ? GROUPS_B / NW : 1;
@@ -58,7 +63,7 @@ struct WideTiling {
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
     static_assert(STAGES * TILE_BYTES <= 160 * 1024, "LDS budget");
     static_assert((STAGES - 2) * LOADS <= 63, "vmcnt range");
-    static_assert(LOADS <= KS, "DMA spread over the score steps");
+    static_assert(LOADS <= KS, "refill spread over the score steps");
 };
 
 template <int NW, int STAGES>
@@ -74,19 +79,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     const int hl = lane & 31;    // head inside the wave's 32
     const int grp = lane >> 5;   // k-slot group (0/1) of the MFMA operand layouts
 
-    // Workgroup -> (chunk k, head group hg).  Blocks go round-robin to the 8
-    // XCDs (block i -> XCD i % 8); all head groups of a chunk share an XCD so
-    // they share its L2 copy of the chunk's tiles.
     int k, hg;
-    if (p.n_hg == 1) {
-        k = blockIdx.x;
-        hg = 0;
-    } else {
-        const int xcd = blockIdx.x & 7;
-        const int slot = blockIdx.x >> 3;
-        k = (slot / p.n_hg) * 8 + xcd;
-        hg = slot % p.n_hg;
-    }
+    block_work(p.n_chunks, p.n_hg, k, hg);
     const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
     const int total = p.plan[0];
     const int chunk = p.plan[1];
@@ -102,32 +96,35 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     const float c2 = p.scale_log2;
 
     // ---- per-lane LDS offsets --------------------------------------------
-    // Score step j reads token row rr = lane & 31, 8 channels starting at
-    // 16j + 8grp: logical 16-byte chunk 2j + grp of region A (j < 32), or
-    // chunk 2(j-32) + grp of region B.
+    // Region A: row r of the tile at r * ROW_A; its 16-byte chunk c sits at
+    // chunk position c + g(r), g(r) = 4 (r & 3) + ((r >> 2) & 3) (a rotation
+    // inside the row's 256 bytes of padding, no wrap-around).  ROW_A is a
+    // multiple of the 256-byte bank width, so a 16-byte read of 16 rows hits
+    // 16 distinct bank groups (g is a permutation of 0..15), and a transposed
+    // read of 4 rows x 4 chunks covers all 16 (g steps by 4 over r & 3).
+    // Every read is a per-lane base plus a compile-time offset.
+    // Score step j < 32 reads row rr = lane & 31, chunk 2j + grp:
+    //   rr * ROW_A + 16 (grp + g(rr)) + 32 j.
+    // Region B (last 128 B of each row): rows of 128 B, chunk c of row r at
+    // position c ^ xb(r); step 32 + j reads chunk 2j + grp:
+    //   kB ^ (j << 5) (the swizzle only touches bits 5-6 of the address).
     const int rr = lane & 31;
-    int koffA[8], koffB[4];
+    const int kA = rr * T::ROW_A + 16 * (grp + rot16(rr));
+    int kB;
     {
-        const int x = M::xa(rr & 15);
         const int xbv = xb(rr & 15);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) koffA[j] = rr * 1024 + (((2 * j + grp) ^ x) << 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) koffB[j] = T::A_BYTES + rr * 128 + (((2 * j + grp) ^ xbv) << 4);
+        kB = T::A_BYTES + rr * 128 + 32 * (xbv >> 1) + 16 * (grp ^ (xbv & 1));
     }
-    // Transposed reads of 16 tokens x 32 columns: this lane supplies 4
-    // columns of token row0 (+8); the instruction hands every lane one column
-    // and 4 tokens.  Columns 32mb + 16((lane>>4)&1) + 4(lane&3) .. +3.
-    int voff0[4], voff1[4];
+    // Transposed reads of 16 tokens x 32 columns: this lane supplies 4 columns
+    // (16((lane>>4)&1) + 4(lane&3) .. +3 of the block) of token row0 (+8); the
+    // instruction hands every lane one column and 4 tokens.  Block (u, mb):
+    //   vA + 16u ROW_A + 64 mb, and the rows 8 further on at
+    //   + 8 ROW_A + 32 (g(row0 + 8) = g(row0) + 2 for row0 < 8).
+    int vA;
     {
         const int row0 = grp * 4 + ((lane & 15) >> 2);
-        const int x0 = M::xa(row0 & 15), x1 = M::xa((row0 + 8) & 15);
         const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            voff0[j] = row0 * 1024 + (((4 * j + cc) ^ x0) << 4) + ((lane & 1) << 3);
-            voff1[j] = (row0 + 8) * 1024 + (((4 * j + cc) ^ x1) << 4) + ((lane & 1) << 3);
-        }
+        vA = row0 * T::ROW_A + 16 * (cc + rot16(row0)) + ((lane & 1) << 3);
     }
 
     while (true) {
@@ -141,19 +138,6 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
         const int slot = pv.base()[r] + split_j;
         const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
         const int n_tiles = (seg_len + T::N - 1) / T::N;
-
-        // Queries (B operand): lane -> head hl, channels 16j + 8grp .. +7 of step j.
-        bf16x8_t qf[T::KS];
-        {
-            const bf16x8_t* qrow =
-                (const bf16x8_t*)(qg + ((size_t)r * p.h + (head_ok ? head : 0)) * kDqk);
-#pragma unroll
-            for (int j = 0; j < T::KS; ++j) {
-                bf16x8_t v = qrow[2 * j + grp];
-                if (!head_ok) v = (bf16x8_t){};
-                qf[j] = v;
-            }
-        }
 
         // DMA instruction `li` (0 .. LOADS-1) of this wave's share of `tile`
         // into stage SC.  Rows past the segment end re-read its last row (the
@@ -169,9 +153,9 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             if (li < T::LOADS_A) {
                 const int row = wave + li * NW;
                 const int srow = min(row, last);
-                const unsigned voff = (unsigned)((lane ^ M::xa(row & 15)) << 4);
+                // the row's 64 chunks land contiguously from position g(row)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc, (LDS_AS void*)(st + row * 1024), 16, voff,
+                    rsrc, (LDS_AS void*)(st + row * T::ROW_A + 16 * rot16(row)), 16, (unsigned)lane << 4,
                     __builtin_amdgcn_readfirstlane(srow * kRowBytesBf16), 0, 0);
             } else {
                 const int gb = wave + (li - T::LOADS_A) * NW;
@@ -187,8 +171,11 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
 #pragma unroll
             for (int li = 0; li < T::LOADS; ++li) issue_load(SC, tile, li);
         };
-        // Wait until this wave's share of tile t has landed: the tiles issued
-        // after it are t+1 .. min(t+STAGES-2, n_tiles-1).
+        // Wait until this wave's share of tile t has landed.  Tile 0 goes out
+        // before the queries, tiles 1 .. STAGES-2 right after them, and step i
+        // refills tile i+STAGES-1, so the tiles issued after t are t+1 ..
+        // min(t+STAGES-2, n_tiles-1) (at step 0 the queries sit between tile 0
+        // and tile 1 and are waited for too, which the first MFMA needs anyway).
         auto wait_tile = [&](int t) {
             const int after = min(STAGES - 2, n_tiles - 1 - t);
             if (STAGES > 3 && after >= 2)
@@ -199,6 +186,23 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
                 wait_vmcnt<0>();
         };
 
+        // Tile 0 first: the queries are as large as a tile, and the first
+        // score MFMA needs both.
+        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
+        // Queries (B operand): lane -> head hl, channels 16j + 8grp .. +7 of step j.
+        // A lane past the last head reads head 0's query instead (finite values,
+        // results never stored), so nothing waits on the loads before the
+        // first score MFMA.
+        bf16x8_t qf[T::KS];
+        {
+            const bf16x8_t* qrow =
+                (const bf16x8_t*)(qg + ((size_t)r * p.h + (head_ok ? head : 0)) * kDqk);
+#pragma unroll
+            for (int j = 0; j < T::KS; ++j) qf[j] = qrow[2 * j + grp];
+        }
+        if (STAGES > 2 && 1 < n_tiles) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
+        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
+
         acc_t o[T::MBLK];
 #pragma unroll
         for (int mb = 0; mb < T::MBLK; ++mb) o[mb] = (acc_t){};
@@ -206,15 +210,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
         float l_run = 0.f;
 
         auto k_frag = [&](lds_byte* tb, int j) -> bf16x8_t {
-            const lds_byte* a = (j < T::KSA) ? tb + koffA[j % 8] + (j / 8) * 256 : tb + koffB[j - T::KSA];
+            const lds_byte* a = (j < T::KSA) ? tb + kA + 32 * j : tb + (kB ^ ((j - T::KSA) << 5));
             return *(const LDS_AS bf16x8_t*)a;
         };
         // Transposed V fragment idx: token half u = idx / MBLK, column block mb = idx % MBLK.
         auto v_frag = [&](lds_byte* tb, int idx) -> bf16x8_t {
             const int u = idx / T::MBLK, mb = idx % T::MBLK;
-            const int blk = (mb / 4) * 256 + u * 16 * 1024;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff0[mb % 4] + blk));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + voff1[mb % 4] + blk));
+            const int blk = 64 * mb + u * 16 * T::ROW_A;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + vA + blk));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(tb + vA + blk + 8 * T::ROW_A + 32));
             return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
                                            0, 1, 2, 3, 4, 5, 6, 7);
         };
@@ -299,10 +303,6 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             }
         };
 
-        // ---- prologue: tiles 0 .. STAGES-2 in flight ------------------------
-        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
-        if (STAGES > 2 && 1 < n_tiles) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
-        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
         for (int i0 = 0; i0 < n_tiles; i0 += STAGES) {
             step(IC<0>{}, i0);
             if (i0 + 1 < n_tiles) step(IC<1 % STAGES>{}, i0 + 1);
@@ -316,35 +316,22 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
             const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
             // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
-            if (final_out) {
-                __bf16* orow = (__bf16*)p.out + ((size_t)r * p.h + head) * kDc;
+            // a row finished here writes out/lse; otherwise its slot's partial
+            // (normalised, bf16) and partial lse
+            __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
+                                      : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head * kDc;
 #pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
+            for (int mb = 0; mb < T::MBLK; ++mb)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        bf16x4_t v;
-                        v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
-                        v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
-                        v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
-                        v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
-                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
-                    }
-                if (grp == 0) p.lse[(size_t)r * p.h + head] = lse_v;
-            } else {
-                float* prow = p.po + ((size_t)slot * p.h + head) * kDc;
-#pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        f32x4_t v;
-                        v[0] = o[mb][q4 * 4 + 0] * inv;
-                        v[1] = o[mb][q4 * 4 + 1] * inv;
-                        v[2] = o[mb][q4 * 4 + 2] * inv;
-                        v[3] = o[mb][q4 * 4 + 3] * inv;
-                        *(f32x4_t*)(prow + mb * 32 + q4 * 8 + grp * 4) = v;
-                    }
-                if (grp == 0) p.plse[(size_t)slot * p.h + head] = lse_v;
-            }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    bf16x4_t v;
+                    v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
+                    v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
+                    v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
+                    v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+                    *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
+                }
+            if (grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head] = lse_v;
         }
 
         pos = seg_end;
@@ -366,9 +353,9 @@ hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template hipError_t launch_decode_wide<4, 4>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<4, 3>(const DecodeParams&, hipStream_t);
-template hipError_t launch_decode_wide<2, 4>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<4, 2>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<2, 3>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<2, 2>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<1, 3>(const DecodeParams&, hipStream_t);
 

@@ -45,21 +45,22 @@ struct PlanView {
 struct WorkspaceLayout {
     size_t plan_ints;   // int32 elements of the plan
     size_t plse_off;    // byte offset of partial lse  [slots, h] fp32
-    size_t po_off;      // byte offset of partial out  [slots, h, 512] fp32
+    size_t po_off;      // byte offset of partial out  [slots, h, 512] (dtype of the call)
     size_t total;       // bytes
     int max_slots;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline WorkspaceLayout workspace_layout(int b, int h, int n_chunks)
+// part_bytes: bytes per partial-output element (2 for bf16 calls, 4 for fp32).
+inline WorkspaceLayout workspace_layout(int b, int h, int n_chunks, int part_bytes)
 {
     WorkspaceLayout w;
     w.plan_ints = 4 + (size_t)(b + 1) + 2 * (size_t)b + (size_t)n_chunks;
     w.max_slots = n_chunks + b;  // every chunk adds at most one cut inside a row
     w.plse_off = align_up(w.plan_ints * 4, 256);
     w.po_off = align_up(w.plse_off + (size_t)w.max_slots * h * 4, 256);
-    w.total = align_up(w.po_off + (size_t)w.max_slots * h * kDc * 4, 256);
+    w.total = align_up(w.po_off + (size_t)w.max_slots * h * kDc * part_bytes, 256);
     return w;
 }
 
@@ -70,7 +71,7 @@ struct DecodeParams {
     void* out;            // [b,h,512] dtype
     float* lse;           // [b,h]
     float* plse;          // [slots,h]
-    float* po;            // [slots,h,512]
+    void* po;             // [slots,h,512] normalised partial outputs, dtype of the call
     int b, h, t_max;
     int n_chunks;         // chunks per head group
     int n_hg;             // head groups
@@ -81,7 +82,7 @@ struct DecodeParams {
 hipError_t launch_plan(const int32_t* seqlens, int b, int t_max, int n_chunks, int min_chunk,
                        int32_t* plan, hipStream_t stream);
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
-                          const float* po, void* out, float* lse, hipStream_t stream);
+                          const void* po, void* out, float* lse, hipStream_t stream);
 
 // bf16 decode variants.  heads_per_group selects the family; variant picks a
 // tiling inside it (0 = default).  Returns hipErrorInvalidValue if absent.

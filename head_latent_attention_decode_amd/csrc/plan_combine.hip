@@ -96,6 +96,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 __device__ inline void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
+__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ inline float4 load4(const __bf16* p)
+{
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
 __device__ inline void store4(__bf16* p, float4 v)
 {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -113,7 +122,7 @@ __device__ inline void store4(__bf16* p, float4 v)
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ plan, int b,
                                                       int h, const float* __restrict__ plse,
-                                                      const float* __restrict__ po,
+                                                      const OutT* __restrict__ po,
                                                       OutT* __restrict__ out,
                                                       float* __restrict__ lse)
 {
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < ns; ++s) {
         const float w = expf(plse[(size_t)(s0 + s) * h + head] - mx);
-        const float4 x = *reinterpret_cast<const float4*>(po + ((size_t)(s0 + s) * h + head) * kDc + c);
+        const float4 x = load4(po + ((size_t)(s0 + s) * h + head) * kDc + c);
         sum += w;
         acc.x += w * x.x;
         acc.y += w * x.y;
@@ -160,13 +169,15 @@ hipError_t launch_plan(const int32_t* seqlens, int b, int t_max, int n_chunks, i
 }
 
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
-                          const float* po, void* out, float* lse, hipStream_t stream)
+                          const void* po, void* out, float* lse, hipStream_t stream)
 {
     const unsigned grid = (unsigned)b * (unsigned)((h + 1) / 2);
     if (bf16)
-        combine_kernel<__bf16><<<grid, 256, 0, stream>>>(plan, b, h, plse, po, (__bf16*)out, lse);
+        combine_kernel<__bf16><<<grid, 256, 0, stream>>>(plan, b, h, plse, (const __bf16*)po,
+                                                         (__bf16*)out, lse);
     else
-        combine_kernel<float><<<grid, 256, 0, stream>>>(plan, b, h, plse, po, (float*)out, lse);
+        combine_kernel<float><<<grid, 256, 0, stream>>>(plan, b, h, plse, (const float*)po,
+                                                        (float*)out, lse);
     return hipGetLastError();
 }
 

@@ -122,7 +122,9 @@ size_t mla_decode_workspace_bytes(mla_dtype_t dtype, int b, int h, int t_max);
  * L = 0 yields out = 0 and lse = -inf.  Rows at or past L are never read.
  * workspace: device scratch of at least mla_decode_workspace_bytes(dtype, b, h,
  * t_max) bytes, 256-byte aligned, contents need not be initialised; it holds
- * the split plan and the split-KV partial results.
+ * the split plan and the split-KV partial results (each partial output is
+ * normalised and stored in dtype, its log-sum-exp in fp32; the combine
+ * accumulates in fp32).
  * Errors (host side, before any launch): MLA_ERR_INVALID_ARGUMENT for a null
  * or misaligned pointer, b <= 0, h <= 0, t_max < 0, b*t_max >= 2^31, unknown
  * dtype, or softmax_scale not finite or <= 0; MLA_ERR_WORKSPACE_TOO_SMALL.

@@ -47,10 +47,11 @@ def test_abi_version_and_status_strings(mla):
 def test_workspace_bytes_host_only(mla):
     ws = mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
     assert ws > 0 and ws % 256 == 0
-    # partial slots: at least (chunks + rows) * heads * (512 + 1) fp32 plus the plan
-    assert ws >= (8 + 64) * 128 * 513 * 4
+    # partial slots: at least (chunks + rows) * heads * (512 outputs in dtype + one fp32 lse)
+    assert ws >= (8 + 64) * 128 * (512 * 2 + 4)
     n = {"n_chunks": 256, "heads_per_group": 64}
-    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096, n) >= (256 + 64) * 128 * 513 * 4
+    assert mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096, n) >= (256 + 64) * 128 * (512 * 2 + 4)
+    assert mla.mla_decode_workspace_bytes(torch.float32, 64, 16, 4096) >= (8 + 64) * 16 * (512 * 4 + 4)
     assert mla.mla_decode_workspace_bytes(torch.bfloat16, 0, 128, 4096) == 0
     assert mla.mla_decode_workspace_bytes(torch.bfloat16, 4, 0, 4096) == 0
     assert mla.mla_decode_workspace_bytes(torch.bfloat16, 4, 8, -1) == 0
@@ -122,7 +123,7 @@ def test_python_binding_checks_tensors(mla):
 
 def test_decode_kernel_name_host_only(mla):
     # the schedule picks a kernel per head count; the query makes no HIP call
-    assert mla.mla_decode_kernel_name(torch.bfloat16, 128) == "decode_wide_kernel<4, 3>"
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 128) == "decode_wide_kernel<4, 2>"
     assert mla.mla_decode_kernel_name(torch.bfloat16, 16).startswith("decode_bf16_kernel<16,")
     assert mla.mla_decode_kernel_name(torch.float32, 16) == "decode_f32_kernel"
     assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"heads_per_group": 64, "variant": 3}) == \
