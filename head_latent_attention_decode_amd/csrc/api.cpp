@@ -164,7 +164,8 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
 
     hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
     hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(seqlens, b, t_max, s.n_chunks, s.min_chunk, plan, hs);
+    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, plan,
+                               dt == MLA_DTYPE_BF16, out, lse, hs);
     if (e != hipSuccess) return MLA_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
     if (dt == MLA_DTYPE_BF16)

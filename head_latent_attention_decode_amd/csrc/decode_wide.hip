@@ -40,6 +40,8 @@
 namespace mla355 {
 namespace {
 
+constexpr float kLn2 = 0.69314718055994531f;
+
 // Chunk rotation of region-A row r (see the per-lane offsets in the kernel).
 __device__ __forceinline__ int rot16(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
@@ -233,19 +235,28 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             const bool refill = i + STAGES - 1 < n_tiles;
 
             // ---- scores: S^T = K . Q'^T, refill DMA spread over the first steps
-            acc_t sacc = (acc_t){};
-            constexpr int PF = 4;
-            bf16x8_t kring[PF];
+            // (two copies of the loop, with and without the refill, so that no
+            // branch sits between the MFMAs)
+            acc_t sacc;
+            auto scores = [&](auto RF) {
+                constexpr bool REFILL = decltype(RF)::value != 0;
+                constexpr int PF = 4;
+                bf16x8_t kring[PF];
 #pragma unroll
-            for (int j = 0; j < PF; ++j) kring[j] = k_frag(tb, j);
+                for (int j = 0; j < PF; ++j) kring[j] = k_frag(tb, j);
 #pragma unroll
-            for (int j = 0; j < T::KS; ++j) {
-                const bf16x8_t kf = kring[j % PF];
-                if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
-                sacc = M::mma(kf, qf[j], sacc);
-                if (j < T::LOADS && refill) issue_load(IC<SR>{}, i + STAGES - 1, j);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                for (int j = 0; j < T::KS; ++j) {
+                    const bf16x8_t kf = kring[j % PF];
+                    if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
+                    sacc = (j == 0) ? M::mma(kf, qf[j], (acc_t){}) : M::mma(kf, qf[j], sacc);
+                    if (REFILL && j < T::LOADS) issue_load(IC<SR>{}, i + STAGES - 1, j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (refill)
+                scores(IC<1>{});
+            else
+                scores(IC<0>{});
 
             // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
             const int tvalid = __builtin_amdgcn_readfirstlane(seg_len - i * T::N);
@@ -262,7 +273,9 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
                                                              __builtin_bit_cast(unsigned, tm), false, false);
             const float tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
             const float m_new = fmaxf(m_run, tmax);
-            if (__any(m_new > m_run + kRescaleThreshold)) {
+            if (i == 0) {
+                m_run = m_new;  // first tile: nothing accumulated yet
+            } else if (__any(m_new > m_run + kRescaleThreshold)) {
                 const float alpha = exp2_fast(m_run - m_new);
                 l_run *= alpha;
                 // The accumulators live in AGPRs; the empty asm statements pin
@@ -279,13 +292,16 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
                 }
                 m_run = m_new;
             }
+            // probabilities of the first 16 tokens now; those of the second 16
+            // (needed from weighted-sum step MBLK on) between the first MFMAs
             bf16x8_t pb[2];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
+            auto prob = [&](int e) {
                 const float x = exp2_fast(__builtin_fmaf(sacc[e], c2, -m_run));
                 l_run += x;
                 pb[e >> 3][e & 7] = (__bf16)x;
-            }
+            };
+#pragma unroll
+            for (int e = 0; e < 8; ++e) prob(e);
 
             // ---- weighted sum: O^T += V^T . P^T
             constexpr int NPV = 2 * T::MBLK;
@@ -299,6 +315,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
                 const bf16x8_t a = vring[idx % PFV];
                 if (idx + PFV < NPV) vring[idx % PFV] = v_frag(tb, idx + PFV);
                 o[mb] = M::mma(a, pb[u], o[mb]);
+                if (idx < 8) prob(8 + idx);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -311,24 +328,22 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
         }
 
         // ---- segment epilogue ----------------------------------------------
+        // A row finished here writes out/lse; otherwise its slot's partial
+        // (normalised, bf16) and partial lse.
         l_run += __shfl_xor(l_run, 32, 64);
         if (head_ok) {
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-            // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
-            // a row finished here writes out/lse; otherwise its slot's partial
-            // (normalised, bf16) and partial lse
+            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
             __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
                                       : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head * kDc;
+            // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
 #pragma unroll
             for (int mb = 0; mb < T::MBLK; ++mb)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     bf16x4_t v;
-                    v[0] = (__bf16)(o[mb][q4 * 4 + 0] * inv);
-                    v[1] = (__bf16)(o[mb][q4 * 4 + 1] * inv);
-                    v[2] = (__bf16)(o[mb][q4 * 4 + 2] * inv);
-                    v[3] = (__bf16)(o[mb][q4 * 4 + 3] * inv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[mb][q4 * 4 + e] * inv);
                     *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
                 }
             if (grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head] = lse_v;

@@ -22,9 +22,10 @@ constexpr int kRowBytesBf16 = kDqk * 2;  // 1152 B: 72 chunks of 16 B
 // tokens; each chunk (per head group) is one workgroup's work.  A chunk may
 // cover the tail of one row and the head of the next; each (row, chunk)
 // intersection is a "segment" with its own softmax state.  A row cut into
-// several segments writes fp32 partials (normalised output + lse) into
-// numbered slots, merged afterwards by the log-sum-exp combine kernel; a row
-// that lies inside one chunk writes its final output directly.
+// several segments writes partials (normalised output in the dtype of the
+// call, fp32 lse) into numbered slots, merged afterwards by the log-sum-exp
+// combine kernel; a row that lies inside one chunk writes its final output
+// directly.
 //
 // int32 layout (offsets in elements):
 //   [0] total tokens  [1] chunk  [2] n_chunks  [3] unused
@@ -79,8 +80,10 @@ struct DecodeParams {
 };
 
 // Launchers (return hipGetLastError() after the launch).
-hipError_t launch_plan(const int32_t* seqlens, int b, int t_max, int n_chunks, int min_chunk,
-                       int32_t* plan, hipStream_t stream);
+// launch_plan also writes out = 0, lse = -inf for every row with no tokens
+// (no decode workgroup touches such a row).
+hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
+                       int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream);
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream);
 

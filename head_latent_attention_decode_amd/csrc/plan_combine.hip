@@ -14,170 +14,233 @@
 namespace mla355 {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanMaxRowBlocks = 2048;
 
-// Inclusive block scan of one int per thread (Hillis-Steele in LDS).
-__device__ int block_inclusive_scan(int x, int* buf)
+// Inclusive scan across the 64 lanes of a wave.
+__device__ int wave_inclusive_scan(int x)
 {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int y = tid >= off ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    const int r = buf[tid];
-    __syncthreads();
-    return r;
+    return x;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
-                                                            int b, int t_max, int n_chunks,
-                                                            int min_chunk, int32_t* plan)
+__device__ int clamped_len(const int32_t* seqlens, int i, int t_max)
 {
-    __shared__ int buf[kPlanThreads];
-    __shared__ int carry_s;
-    PlanView v{plan, b};
+    const int L = seqlens[i];
+    return L < 0 ? 0 : (L > t_max ? t_max : L);
+}
+
+// Workgroup 0, wave 0 builds the plan (two scans over the clamped lengths, 64
+// rows per step).  Workgroups 1.. give every row with no tokens out = 0 and
+// lse = -inf.
+template <typename OutT>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
+                                                            int b, int h, int t_max, int n_chunks,
+                                                            int min_chunk, int32_t* plan,
+                                                            OutT* out, float* lse)
+{
     const int tid = threadIdx.x;
+    if (blockIdx.x > 0) {
+        for (int r = blockIdx.x - 1; r < b; r += gridDim.x - 1) {
+            if (clamped_len(seqlens, r, t_max) != 0) continue;
+            OutT* o = out + (size_t)r * h * kDc;
+            for (int i = tid; i < h * kDc; i += kPlanThreads) o[i] = (OutT)0.f;
+            for (int i = tid; i < h; i += kPlanThreads) lse[(size_t)r * h + i] = -INFINITY;
+        }
+        return;
+    }
+    if (tid >= 64) return;
+    PlanView v{plan, b};
+    const int lane = tid;
 
     // Pass 1: cu[] = prefix sums of the clamped lengths.
     int carry = 0;
-    if (tid == 0) v.cu()[0] = 0;
-    for (int base = 0; base < b; base += kPlanThreads) {
-        const int i = base + tid;
-        int L = 0;
-        if (i < b) {
-            L = seqlens[i];
-            L = L < 0 ? 0 : (L > t_max ? t_max : L);
-        }
-        const int inc = block_inclusive_scan(L, buf);
+    if (lane == 0) v.cu()[0] = 0;
+    for (int base = 0; base < b; base += 64) {
+        const int i = base + lane;
+        const int L = i < b ? clamped_len(seqlens, i, t_max) : 0;
+        const int inc = wave_inclusive_scan(L);
         if (i < b) v.cu()[i + 1] = carry + inc;
-        if (tid == kPlanThreads - 1) carry_s = inc;
-        __syncthreads();
-        carry += carry_s;
-        __syncthreads();
+        carry += __shfl(inc, 63, 64);
     }
     const int total = carry;
     int chunk = (int)(((long long)total + n_chunks - 1) / n_chunks);
     if (chunk < min_chunk) chunk = min_chunk;
-    if (tid == 0) {
+    if (lane == 0) {
         plan[0] = total;
         plan[1] = chunk;
         plan[2] = n_chunks;
         plan[3] = 0;
     }
-    for (int k = tid; k < n_chunks; k += kPlanThreads) v.chunk_row()[k] = -1;
-    __syncthreads();
+    // Chunks starting at or past the last token are idle.  Every other chunk
+    // k starts inside exactly one non-empty row (the one holding token
+    // k * chunk), written in pass 2; the two sets are disjoint.
+    const int first_idle = (total + chunk - 1) / chunk;
+    for (int k = first_idle + lane; k < n_chunks; k += 64) v.chunk_row()[k] = -1;
 
-    // Pass 2: segments per row, first partial slot per row, and for every
-    // chunk the row holding its first token.
+    // Pass 2 (the lengths are scanned again rather than read back): segments
+    // per row, first partial slot per row, and the starting row of every chunk.
     carry = 0;
-    for (int base = 0; base < b; base += kPlanThreads) {
-        const int i = base + tid;
-        int ns = 0;
-        if (i < b) {
-            const int lo = v.cu()[i], hi = v.cu()[i + 1];
-            if (hi > lo) {
-                ns = (hi - 1) / chunk - lo / chunk + 1;
-                for (int k = (lo + chunk - 1) / chunk; k * chunk < hi; ++k) v.chunk_row()[k] = i;
-            }
-            v.nsplit()[i] = ns;
+    int slots = 0;
+    for (int base = 0; base < b; base += 64) {
+        const int i = base + lane;
+        const int L = i < b ? clamped_len(seqlens, i, t_max) : 0;
+        const int inc = wave_inclusive_scan(L);
+        const int hi = carry + inc, lo = hi - L;
+        int ns = 0, k_lo = 0, k_hi = 0;  // chunks k_lo .. k_hi-1 start inside row i
+        if (i < b && L > 0) {
+            ns = (hi - 1) / chunk - lo / chunk + 1;
+            k_lo = (int)(((long long)lo + chunk - 1) / chunk);
+            k_hi = (int)(((long long)hi + chunk - 1) / chunk);
         }
-        const int inc = block_inclusive_scan(ns, buf);
-        if (i < b) v.base()[i] = carry + inc - ns;
-        if (tid == kPlanThreads - 1) carry_s = inc;
-        __syncthreads();
-        carry += carry_s;
-        __syncthreads();
+        // a lane writes its own row's few chunk starts; rows holding many are
+        // written by the whole wave, one row at a time
+        constexpr int kLaneChunks = 4;
+        if (k_hi - k_lo <= kLaneChunks)
+            for (int k = k_lo; k < k_hi; ++k) v.chunk_row()[k] = i;
+        unsigned long long many = __ballot(k_hi - k_lo > kLaneChunks);
+        while (many) {
+            const int j = __builtin_ctzll(many);
+            many &= many - 1;
+            const int a = __shfl(k_lo, j, 64), z = __shfl(k_hi, j, 64);
+            for (int k = a + lane; k < z; k += 64) v.chunk_row()[k] = base + j;
+        }
+        const int ns_inc = wave_inclusive_scan(ns);
+        if (i < b) {
+            v.nsplit()[i] = ns;
+            v.base()[i] = slots + ns_inc - ns;
+        }
+        carry += __shfl(inc, 63, 64);
+        slots += __shfl(ns_inc, 63, 64);
     }
 }
 
-__device__ inline void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 
-__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
-__device__ inline float4 load4(const __bf16* p)
+__device__ inline void load8(const float* p, float (&x)[8])
 {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 c = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
 }
 
-__device__ inline void store4(__bf16* p, float4 v)
+__device__ inline void load8(const __bf16* p, float (&x)[8])
 {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 o;
-    o[0] = (__bf16)v.x;
-    o[1] = (__bf16)v.y;
-    o[2] = (__bf16)v.z;
-    o[3] = (__bf16)v.w;
-    *reinterpret_cast<bf16x4*>(p) = o;
+    const bf16x8_v v = *reinterpret_cast<const bf16x8_v*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
 }
 
-// One workgroup: two heads of one batch row; 128 threads per head, 4 latent
-// columns per thread.  Rows with one segment were finished by the decode
-// kernel; rows with none get out = 0, lse = -inf.
+__device__ inline void store8(float* p, const float (&x)[8])
+{
+    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+__device__ inline void store8(__bf16* p, const float (&x)[8])
+{
+    bf16x8_v v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    *reinterpret_cast<bf16x8_v*>(p) = v;
+}
+
+constexpr int kCombineThreads = 256;  // 4 waves = 4 heads of one batch row
+constexpr int kCombineUnroll = 8;     // partial rows in flight per wave
+
+// One wave per (batch row, head) of a row cut into several segments; no LDS
+// and no barrier.  Lane j first holds the lse of slots j, j+64, ... (max and
+// sum by shuffles), then every partial row (512 columns) is one coalesced
+// load, lane l taking columns 8l .. 8l+7, kCombineUnroll rows in flight; the
+// weight of slot s is read from the lane that holds it.  Rows with one
+// segment were finished by the decode kernel, rows with none by plan_kernel.
 template <typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ plan, int b,
-                                                      int h, const float* __restrict__ plse,
-                                                      const OutT* __restrict__ po,
-                                                      OutT* __restrict__ out,
-                                                      float* __restrict__ lse)
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t* __restrict__ plan,
+                                                                  int b, int h,
+                                                                  const float* __restrict__ plse,
+                                                                  const OutT* __restrict__ po,
+                                                                  OutT* __restrict__ out,
+                                                                  float* __restrict__ lse)
 {
     PlanView v{const_cast<int32_t*>(plan), b};
-    const int hpairs = (h + 1) / 2;
-    const int r = blockIdx.x / hpairs;
-    const int head = (blockIdx.x % hpairs) * 2 + (threadIdx.x >> 7);
-    if (r >= b || head >= h) return;
-    const int c = (threadIdx.x & 127) * 4;
+    const int groups = (h + 3) / 4;
+    const int r = blockIdx.x / groups;
+    const int head = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (head >= h) return;
     const int ns = v.nsplit()[r];
-    if (ns == 1) return;
-    OutT* o = out + ((size_t)r * h + head) * kDc + c;
-    if (ns == 0) {
-        store4(o, make_float4(0.f, 0.f, 0.f, 0.f));
-        if (c == 0) lse[(size_t)r * h + head] = -INFINITY;
-        return;
-    }
+    if (ns <= 1) return;
     const int s0 = v.base()[r];
-    float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, plse[(size_t)(s0 + s) * h + head]);
-    float sum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < ns; ++s) {
-        const float w = expf(plse[(size_t)(s0 + s) * h + head] - mx);
-        const float4 x = load4(po + ((size_t)(s0 + s) * h + head) * kDc + c);
-        sum += w;
-        acc.x += w * x.x;
-        acc.y += w * x.y;
-        acc.z += w * x.z;
-        acc.w += w * x.w;
+    const float* pl = plse + (size_t)s0 * h + head;
+
+    float m = -INFINITY;
+    for (int s = lane; s < ns; s += 64) m = fmaxf(m, pl[(size_t)s * h]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float sm = 0.f;
+    for (int s = lane; s < ns; s += 64) sm += expf(pl[(size_t)s * h] - m);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off, 64);
+    const float inv = 1.0f / sm;
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int sb = 0; sb < ns; sb += 64) {
+        // normalised weight of slot sb + lane, held by that lane
+        const float wl = sb + lane < ns ? expf(pl[(size_t)(sb + lane) * h] - m) * inv : 0.f;
+        const int nb = min(64, ns - sb);
+        for (int s = 0; s < nb; s += kCombineUnroll) {
+            float x[kCombineUnroll][8];
+#pragma unroll
+            for (int u = 0; u < kCombineUnroll; ++u) {
+                const int sl = sb + min(s + u, nb - 1);
+                load8(po + ((size_t)(s0 + sl) * h + head) * kDc + 8 * lane, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kCombineUnroll; ++u) {
+                // slots past the end re-read the last one with weight 0
+                const float w = s + u < nb ? __shfl(wl, s + u, 64) : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += w * x[u][e];
+            }
+        }
     }
-    const float inv = 1.0f / sum;
-    store4(o, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
-    if (c == 0) lse[(size_t)r * h + head] = mx + logf(sum);
+    store8(out + ((size_t)r * h + head) * kDc + 8 * lane, acc);
+    if (lane == 0) lse[(size_t)r * h + head] = m + logf(sm);
 }
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* seqlens, int b, int t_max, int n_chunks, int min_chunk,
-                       int32_t* plan, hipStream_t stream)
+hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
+                       int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream)
 {
-    plan_kernel<<<1, kPlanThreads, 0, stream>>>(seqlens, b, t_max, n_chunks, min_chunk, plan);
+    const unsigned grid = 1u + (unsigned)(b < kPlanMaxRowBlocks ? b : kPlanMaxRowBlocks);
+    if (bf16)
+        plan_kernel<__bf16><<<grid, kPlanThreads, 0, stream>>>(seqlens, b, h, t_max, n_chunks, min_chunk,
+                                                               plan, (__bf16*)out, lse);
+    else
+        plan_kernel<float><<<grid, kPlanThreads, 0, stream>>>(seqlens, b, h, t_max, n_chunks, min_chunk,
+                                                              plan, (float*)out, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)b * (unsigned)((h + 1) / 2);
+    const unsigned grid = (unsigned)b * (unsigned)((h + 3) / 4);
     if (bf16)
-        combine_kernel<__bf16><<<grid, 256, 0, stream>>>(plan, b, h, plse, (const __bf16*)po,
-                                                         (__bf16*)out, lse);
+        combine_kernel<__bf16><<<grid, kCombineThreads, 0, stream>>>(plan, b, h, plse, (const __bf16*)po,
+                                                                     (__bf16*)out, lse);
     else
-        combine_kernel<float><<<grid, 256, 0, stream>>>(plan, b, h, plse, (const float*)po,
-                                                        (float*)out, lse);
+        combine_kernel<float><<<grid, kCombineThreads, 0, stream>>>(plan, b, h, plse, (const float*)po,
+                                                                    (float*)out, lse);
     return hipGetLastError();
 }
 

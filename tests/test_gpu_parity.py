@@ -95,7 +95,7 @@ def _case_id(c):
 @pytest.mark.parametrize("h,cfg", BF16_CASES, ids=[_case_id(c) for c in BF16_CASES])
 def test_bf16_edges_every_output(mla, h, cfg):
     w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=100 + h, device="cuda")
-    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}):
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
         c = dict(cfg or {})
         c.update(extra)
         out, lse = _run(mla, w, c or None)
@@ -143,6 +143,56 @@ def test_bf16_closed_forms(mla):
     shift = (w.q_prime[:, :, 575].float() - q575_before).cpu().double().numpy()
     assert_out(to_np(out1), to_np(out0), BF16_OUT_REL, "out under shift")
     np.testing.assert_allclose(to_np(lse1 - lse0), SCALE * shift, atol=2e-3)
+
+
+def test_bf16_combine_many_segments(mla):
+    # two long rows cut into ~40 segments each (several rounds of the combine's
+    # per-wave slot loop); 100 heads leave the last 32-head group partly empty
+    w = workloads.make_custom(3, 100, [20000, 13001, 5], seed=21, device="cuda")
+    heads = [0, 31, 32, 63, 64, 95, 96, 99]
+    out, lse = _run(mla, w, {"n_chunks": 96})
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b), heads)
+
+
+def _plan_model(lens, t_max, n_chunks, min_chunk):
+    """The split rule written out in Python: the batch as one concatenated
+    token sequence cut into n_chunks equal chunks (at least min_chunk tokens)."""
+    L = [min(max(x, 0), t_max) for x in lens]
+    cu = [0]
+    for x in L:
+        cu.append(cu[-1] + x)
+    total = cu[-1]
+    chunk = max(-(-total // n_chunks), min_chunk)
+    ns = [((cu[i + 1] - 1) // chunk - cu[i] // chunk + 1) if L[i] > 0 else 0 for i in range(len(L))]
+    base = [sum(ns[:i]) for i in range(len(L))]
+    row_of = []
+    for k in range(n_chunks):
+        t = k * chunk
+        row_of.append(next(i for i in range(len(L)) if cu[i] <= t < cu[i + 1]) if t < total else -1)
+    return [total, chunk, n_chunks, 0] + cu + base + ns + row_of
+
+
+@pytest.mark.parametrize("lens", [
+    [4096] * 64,                                    # uniform: four chunks per row
+    [131072] * 4,                                   # long rows: 64 chunk starts per row
+    [0, 5, 0, 700, 33, 0, 9000, 1] + [17] * 120,    # ragged, empty rows, b > 64
+    [0, 0, 0],                                      # nothing to attend
+    [-3, 10**9, 40],                                # out-of-range lengths are clamped
+], ids=["uniform", "long", "ragged", "empty", "clamped"])
+def test_plan_bit_exact(mla, lens):
+    # the plan sits at the start of the workspace; integer data, compared exactly
+    b, h = len(lens), 128
+    t_max = min(max(max(lens), 1), 131072)
+    cache = torch.zeros(b, t_max, 576, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(b, h, 576, dtype=torch.bfloat16, device="cuda")
+    seqlens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(mla.mla_decode_workspace_bytes(torch.bfloat16, b, h, t_max), dtype=torch.uint8,
+                     device="cuda")
+    mla.mla_decode(q, cache, seqlens, SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    ref = _plan_model(lens, t_max, 256, 32)
+    got = ws[:4 * len(ref)].cpu().view(torch.int32).tolist()
+    assert got == ref
 
 
 # ---------------------------------------------------------------- absorbs, bf16
