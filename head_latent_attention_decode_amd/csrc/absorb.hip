@@ -8,13 +8,13 @@
 //             the 512-wide attention output.
 // Both are per-head products with a 128 x 512 weight block used by only b
 // query rows, so they are weight-read bound at small b.  bf16: one workgroup
-// per (head, 64 output columns) stages that weight slab in LDS once, reads
-// it transposed (ds_read_b64_tr_b16) as the A operand of
-// v_mfma_f32_16x16x32_bf16, and streams the b input rows as the B operand
-// (contraction dimension contiguous in memory), fp32 accumulation.  fp32: the
-// vector-ALU kernels below (IEEE fp32 FMAs), one workgroup per (head, block of
-// 16 batch rows).
-#include "mla355_internal.h"
+// per (head, 64 output columns) DMAs that weight slab and the head's input
+// rows (64 at a time) into LDS with every byte in flight at once, reads the
+// slab transposed (ds_read_b64_tr_b16) as the A operand of
+// v_mfma_f32_16x16x32_bf16 and the input rows as the B operand, fp32
+// accumulation.  fp32: the vector-ALU kernels below (IEEE fp32 FMAs), one
+// workgroup per (head, block of 16 batch rows).
+#include "bf16_common.h"
 
 namespace mla355 {
 namespace {
@@ -126,97 +126,150 @@ __global__ __launch_bounds__(128) void absorb_o_kernel(int b, int h, const T* __
 }
 
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
-
 // Weight slab [KD][64] bf16 in LDS, 128-byte rows.  16-byte chunk c of row r is
 // stored at c ^ (2 * f(r)), f(r) = ((r >> 1) & 1) | (((r >> 3) & 1) << 1), so the
 // transposed reads of 4-row groups spread over distinct 32-byte bank windows.
-__device__ __forceinline__ int slab_off(int r, int c)
+__device__ __forceinline__ int slab_chunk(int r, int c)
 {
     const int f = ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
-    return r * 128 + ((c ^ (2 * f)) << 4);
+    return c ^ (2 * f);
 }
 
 // Y^T[n, m] = sum_k W[h][k][n] X[m][h][k] for 64 columns n0.. of head h.
 //   W  [H][KD][ND] (n contiguous)      X  row m of head h at x + m*x_rs + h*KD
 //   Y  row m of head h at y + m*y_rs + h*y_hs + n
-// 4 waves; wave w owns columns n0 + 16w .. +15 (MFMA A rows); batch rows are
-// the MFMA B columns, 16 per block.  When rope != nullptr (q absorb), the
-// workgroups of column block 0 also copy rope[m][h][0:64] to y[...][ND:ND+64].
-template <int KD, int ND>
+// Both operands go HBM -> LDS by direct-to-LDS DMA, all of a block's bytes in
+// flight at once (the product is bound by reading the weights): the weight
+// slab W[h][:, n0:n0+64] once, then the head's input rows 64 at a time
+// (16-byte chunk c of staged row m at c ^ (m & 15), so 16 consecutive rows
+// read at one k offset hit 16 distinct bank quads).  4 waves; wave w owns
+// columns n0 + 16w .. +15 (v_mfma_f32_16x16x32_bf16 A rows, read transposed
+// with ds_read_b64_tr_b16); batch rows are the B columns, 16 per block.  When
+// rope != nullptr (q absorb), the workgroups of column block 0 also copy
+// rope[m][h][0:64] to y[...][ND:ND+64].
+template <int KD, int ND, int NCB>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __bf16* __restrict__ x,
                                                           long x_rs, const __bf16* __restrict__ w,
                                                           __bf16* __restrict__ y, long y_rs, int y_hs,
                                                           const __bf16* __restrict__ rope)
 {
-    constexpr int NB = ND / 64;
+    constexpr int NB = ND / (64 * NCB);       // workgroups per head
     constexpr int KSTEPS = KD / 32;
-    __shared__ __attribute__((aligned(16))) unsigned char slab[KD * 128];
+    constexpr int W_BYTES = NCB * KD * 128;   // NCB slabs [KD][64]
+    constexpr int X_ROW = KD * 2;             // bytes of one staged input row
+    constexpr int X_BYTES = 64 * X_ROW;       // 64 input rows per block
+    constexpr int W_DMA = W_BYTES / 4096;     // 1 KB DMA instructions per wave
+    constexpr int X_DMA = X_BYTES / 4096;
+    static_assert(W_BYTES % 4096 == 0 && X_BYTES % 4096 == 0, "whole DMA rounds per wave");
+    static_assert(ND % (64 * NCB) == 0, "whole slabs per workgroup");
+    static_assert(X_ROW >= 256, "16 chunks per staged row for the swizzle");
+    lds_byte* slab = stage_lds<W_BYTES, 0>();
+    lds_byte* xs = stage_lds<X_BYTES, 1>();
     const int h = blockIdx.x / NB;
-    const int n0 = (blockIdx.x % NB) * 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = (blockIdx.x % NB) * 64 * NCB;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // stage W[h][:, n0:n0+64] (KD rows x 8 chunks of 16 B)
-    const __bf16* wh = w + (size_t)h * KD * ND + n0;
-#pragma unroll 4
-    for (int i = tid; i < KD * 8; i += 256) {
-        const int r = i >> 3, c = i & 7;
-        const bf16x8_t v = *(const bf16x8_t*)(wh + (size_t)r * ND + c * 8);
-        *(LDS_AS bf16x8_t*)((LDS_AS unsigned char*)slab + slab_off(r, c)) = v;
+    // weight slabs (columns n0 + 64cb ..): DMA block j = rows 8(j % (KD/8)) ..
+    // +7 of slab j / (KD/8); lane -> row + lane/8, slot lane%8
+    {
+        const __bf16* wh = w + (size_t)h * KD * ND + n0;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)wh, (short)0, ((KD - 1) * ND + 64 * NCB) * 2, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < W_DMA; ++i) {
+            const int j = wave * W_DMA + i;
+            const int cb = j / (KD / 8);
+            const int r = (j % (KD / 8)) * 8 + (lane >> 3);
+            const int c = slab_chunk(r, lane & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(slab + j * 1024), 16,
+                                                     (unsigned)((r * ND + cb * 64 + c * 8) * 2), 0, 0, 0);
+        }
     }
+    const __bf16* xh = x + (size_t)h * KD;
+    const unsigned x_bytes = (unsigned)(((size_t)(M - 1) * x_rs + KD) * 2);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xh, (short)0, x_bytes, kBufferFlags);
+    // input rows mb0*64 .. +63 (rows past M re-read row M-1; never stored)
+    auto stage_x = [&](int mb0) {
+#pragma unroll
+        for (int i = 0; i < X_DMA; ++i) {
+            const int j = wave * X_DMA + i;
+            const int byte = j * 1024 + lane * 16;
+            const int m = byte / X_ROW;
+            const int c = ((byte % X_ROW) >> 4) ^ (m & 15);
+            const int mg = min(mb0 * 64 + m, M - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (LDS_AS void*)(xs + j * 1024), 16,
+                                                     (unsigned)(((size_t)mg * x_rs + c * 8) * 2), 0, 0, 0);
+        }
+    };
+    stage_x(0);
     if (rope != nullptr && n0 == 0) {
-        for (int i = tid; i < M * 8; i += 256) {
+        for (int i = threadIdx.x; i < M * 8; i += 256) {
             const int m = i >> 3, c = i & 7;
             const bf16x8_t v = *(const bf16x8_t*)(rope + ((size_t)m * H + h) * 64 + c * 8);
             *(bf16x8_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + ND + c * 8) = v;
         }
     }
+    wait_vmcnt<0>();
     __syncthreads();
 
-    // A operand (W^T rows n, k-slots g*8 .. +7) for every k step, read once.
+    // A operand (W^T rows n, k-slots g*8 .. +7) for every k step of a slab.
     // tr16 mapping: source lane s of a 16-lane group supplies row k0 + g*8 + s/4
     // (+4 for the upper half), columns 4*(s%4) .. +3 of the wave's 16 columns.
     const int g = lane >> 4, s = lane & 15;
     const int col = wave * 16 + 4 * (s & 3);
-    bf16x8_t a[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int r0 = ks * 32 + g * 8 + (s >> 2);
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)((LDS_AS unsigned char*)slab + slab_off(r0, col >> 3) + (col & 7) * 2));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)((LDS_AS unsigned char*)slab + slab_off(r0 + 4, col >> 3) + (col & 7) * 2));
-        a[ks] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                        0, 1, 2, 3, 4, 5, 6, 7);
-    }
-
-    // B operand: X rows (batch rows m = mb*16 + s), k-slots g*8 .. +7.
-    for (int mb = 0; mb * 16 < M; ++mb) {
-        const int m = mb * 16 + s;
-        const bool ok = m < M;
-        const __bf16* xr = x + (size_t)(ok ? m : 0) * x_rs + (size_t)h * KD + g * 8;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto read_a = [&](int cb, bf16x8_t (&a)[KSTEPS]) {
+        const lds_byte* sl = slab + cb * KD * 128;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            bf16x8_t b = *(const bf16x8_t*)(xr + ks * 32);
-            if (!ok) b = (bf16x8_t){};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc, 0, 0, 0);
+            const int r0 = ks * 32 + g * 8 + (s >> 2);
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4_t*)(sl + r0 * 128 + (slab_chunk(r0, col >> 3) << 4) + (col & 7) * 2));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4_t*)(sl + (r0 + 4) * 128 + (slab_chunk(r0 + 4, col >> 3) << 4) + (col & 7) * 2));
+            a[ks] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
         }
-        // acc[i]: output column n0 + 16*wave + g*4 + i of batch row m
-        if (ok) {
-            bf16x4_t o;
-            o[0] = (__bf16)acc[0];
-            o[1] = (__bf16)acc[1];
-            o[2] = (__bf16)acc[2];
-            o[3] = (__bf16)acc[3];
-            *(bf16x4_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + wave * 16 + g * 4) = o;
+    };
+    bf16x8_t a[KSTEPS];
+    if (NCB == 1) read_a(0, a);
+
+    for (int mb0 = 0; mb0 * 64 < M; ++mb0) {
+        if (mb0 > 0) {
+            __syncthreads();  // every wave is done with the previous block
+            stage_x(mb0);
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            if (NCB > 1) read_a(cb, a);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                // B operand: staged row mb*16 + s, k-slots g*8 .. +7 of step ks
+                const lds_byte* xr = xs + (mb * 16 + s) * X_ROW;
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const bf16x8_t b = *(const LDS_AS bf16x8_t*)(xr + (((ks * 4 + g) ^ s) << 4));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc, 0, 0, 0);
+                }
+                // acc[i]: output column n0 + 64cb + 16*wave + g*4 + i of batch row m
+                const int m = mb0 * 64 + mb * 16 + s;
+                if (m < M) {
+                    bf16x4_t o;
+                    o[0] = (__bf16)acc[0];
+                    o[1] = (__bf16)acc[1];
+                    o[2] = (__bf16)acc[2];
+                    o[3] = (__bf16)acc[3];
+                    *(bf16x4_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + cb * 64 + wave * 16 + g * 4) = o;
+                }
+            }
         }
     }
 }
+
+constexpr int kAbsorbQSlabs = 4;  // 64-column weight slabs per q-absorb workgroup
 
 }  // namespace
 
@@ -225,7 +278,7 @@ hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const vo
 {
     const unsigned grid = (unsigned)h * (unsigned)((b + kRows - 1) / kRows);
     if (bf16)
-        absorb_mfma_kernel<kDk, kDc><<<h * (kDc / 64), 256, 0, stream>>>(
+        absorb_mfma_kernel<kDk, kDc, kAbsorbQSlabs><<<h * (kDc / (64 * kAbsorbQSlabs)), 256, 0, stream>>>(
             b, h, (const __bf16*)q_nope, (long)h * kDk, (const __bf16*)w_uk, (__bf16*)q_prime,
             (long)h * kDqk, kDqk, (const __bf16*)q_rope);
     else
@@ -240,7 +293,7 @@ hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w
 {
     const unsigned grid = (unsigned)h * (unsigned)((b + kRows - 1) / kRows);
     if (bf16)
-        absorb_mfma_kernel<kDc, kDv><<<h * (kDv / 64), 256, 0, stream>>>(
+        absorb_mfma_kernel<kDc, kDv, 1><<<h * (kDv / 64), 256, 0, stream>>>(
             b, h, (const __bf16*)o, (long)h * kDc, (const __bf16*)w_uv, (__bf16*)y, (long)h * kDv,
             kDv, nullptr);
     else

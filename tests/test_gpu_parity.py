@@ -197,10 +197,12 @@ def test_plan_bit_exact(mla, lens):
 
 # ---------------------------------------------------------------- absorbs, bf16
 
-def test_absorbs_bf16(mla):
-    q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(64, 128, device="cuda")
+@pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8)])
+def test_absorbs_bf16(mla, b, h):
+    # b = 100: two rounds of the 64-row load groups, the second one ragged
+    q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(b, h, device="cuda")
     qp = mla.mla_absorb_q(q_nope, w_uk, q_rope)
-    o = torch.randn(64, 128, 512, device="cuda").to(torch.bfloat16)
+    o = torch.randn(b, h, 512, device="cuda").to(torch.bfloat16)
     y = mla.mla_absorb_o(o, w_uv)
     torch.cuda.synchronize()
     ref_q = oracle.absorb_q(q_nope.cpu(), w_uk.cpu(), q_rope.cpu())
