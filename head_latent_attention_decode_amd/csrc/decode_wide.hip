@@ -84,9 +84,11 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     int k, hg;
     block_work(p.n_chunks, p.n_hg, k, hg);
     const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
-    const int total = p.plan[0];
-    const int chunk = p.plan[1];
-    int r = pv.chunk_row()[k];
+    // plan entries are the same for every lane: keep them in scalar registers
+    auto plan_at = [](const int32_t* q) { return __builtin_amdgcn_readfirstlane(*q); };
+    const int total = plan_at(p.plan);
+    const int chunk = plan_at(p.plan + 1);
+    int r = plan_at(pv.chunk_row() + k);
     if (r < 0) return;
     int pos = k * chunk;
     const int end = pos + min(chunk, total - pos);
@@ -130,14 +132,14 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     }
 
     while (true) {
-        const int row_lo = pv.cu()[r];
-        const int row_hi = pv.cu()[r + 1];
+        const int row_lo = plan_at(pv.cu() + r);
+        const int row_hi = plan_at(pv.cu() + r + 1);
         const int seg_end = min(end, row_hi);
         const int seg_a = pos - row_lo;
         const int seg_len = seg_end - pos;
         const int split_j = k - row_lo / chunk;
-        const bool final_out = pv.nsplit()[r] == 1;
-        const int slot = pv.base()[r] + split_j;
+        const bool final_out = plan_at(pv.nsplit() + r) == 1;
+        const int slot = plan_at(pv.base() + r) + split_j;
         const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
         const int n_tiles = (seg_len + T::N - 1) / T::N;
 
@@ -331,29 +333,38 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
         // A row finished here writes out/lse; otherwise its slot's partial
         // (normalised, bf16) and partial lse.
         l_run += __shfl_xor(l_run, 32, 64);
-        if (head_ok) {
-            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-            __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
-                                      : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head * kDc;
-            // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
+        {
+            // The lane's head and column group are derived again here from the
+            // thread index (opaque to the compiler) instead of being kept live
+            // across the tile loop, where every register is taken.
+            int tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const int e_grp = (tid >> 5) & 1;
+            const int e_head = hg * T::HG + wave * 32 + (tid & 31);
+            if (e_head < p.h) {
+                const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+                const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+                __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
+                                          : (__bf16*)p.po + (size_t)slot * p.h * kDc) + e_head * kDc + e_grp * 4;
+                // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
 #pragma unroll
-            for (int mb = 0; mb < T::MBLK; ++mb)
+                for (int mb = 0; mb < T::MBLK; ++mb)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    bf16x4_t v;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        bf16x4_t v;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[mb][q4 * 4 + e] * inv);
-                    *(bf16x4_t*)(orow + mb * 32 + q4 * 8 + grp * 4) = v;
-                }
-            if (grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head] = lse_v;
+                        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[mb][q4 * 4 + e] * inv);
+                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8) = v;
+                    }
+                if (e_grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[e_head] = lse_v;
+            }
         }
 
         pos = seg_end;
         if (pos >= end) break;
         wg_barrier();  // every wave is done with the stages before they are refilled
         ++r;
-        while (pv.cu()[r + 1] <= pos) ++r;
+        while (plan_at(pv.cu() + r + 1) <= pos) ++r;
     }
 }
 
