@@ -856,6 +856,7 @@ const VariantEntry kVariants[] = {
     {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>"},
     {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3>"},
     {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2>"},
+    {128, 5, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4>"},
     {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3>"},
     {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2>"},
     {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3>"},

@@ -18,7 +18,7 @@
 //  * Tiles of 32 latent rows stream HBM -> LDS with direct-to-LDS 16-byte DMA
 //    (STAGES-deep ring, STAGES-1 tiles in flight).  A tile is stored as
 //    region A = the first 1024 B of each row (one DMA instruction per row,
-//    rows padded to 1280 B) and region B = the last 128 B (8 rows per
+//    rows padded to 1152 B) and region B = the last 128 B (8 rows per
 //    instruction); see the per-lane offsets below for the swizzles.  The
 //    refill DMA of a tile is spread over the first score MFMAs rather than
 //    issued as one burst.
@@ -43,14 +43,14 @@ namespace {
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Chunk rotation of region-A row r (see the per-lane offsets in the kernel).
-__device__ __forceinline__ int rot16(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int rot16(int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); }
 
 template <int NW, int STAGES>
 struct WideTiling {
     static constexpr int THREADS = NW * 64;
     static constexpr int HG = 32 * NW;                 // heads per workgroup
     static constexpr int N = 32;                       // tokens per tile
-    static constexpr int ROW_A = 1024 + 256;              // LDS stride of a region-A row (rotated)
+    static constexpr int ROW_A = 1024 + 128;              // LDS stride of a region-A row (rotated)
     static constexpr int A_BYTES = N * ROW_A;
     static constexpr int TILE_BYTES = A_BYTES + N * 128;  // + region B
     static constexpr int LOADS_A = N / NW;             // region-A DMA instructions per wave
@@ -100,13 +100,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     const float c2 = p.scale_log2;
 
     // ---- per-lane LDS offsets --------------------------------------------
-    // Region A: row r of the tile at r * ROW_A; its 16-byte chunk c sits at
-    // chunk position c + g(r), g(r) = 4 (r & 3) + ((r >> 2) & 3) (a rotation
-    // inside the row's 256 bytes of padding, no wrap-around).  ROW_A is a
-    // multiple of the 256-byte bank width, so a 16-byte read of 16 rows hits
-    // 16 distinct bank groups (g is a permutation of 0..15), and a transposed
-    // read of 4 rows x 4 chunks covers all 16 (g steps by 4 over r & 3).
-    // Every read is a per-lane base plus a compile-time offset.
+    // Region A: row r of the tile at r * ROW_A (ROW_A = 1152 B = 72 16-byte
+    // bank quads, so row r starts at quad 8 (r & 1) of the 16 quads of a
+    // 256-byte bank cycle); its 16-byte chunk c sits at chunk position
+    // c + g(r), g(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3) (inside the row's
+    // 128 bytes of padding, no wrap-around).  Row r's chunk c then starts at
+    // quad 8 (r & 1) + 4 ((r >> 1) & 1) + ((r >> 2) & 3) + c (mod 16), distinct
+    // over any 16 consecutive rows for a 16-byte read, and the transposed reads
+    // (4 rows x 4 chunks per 32 lanes) cover all 64 banks once.  Every read is
+    // a per-lane base plus a compile-time offset.
     // Score step j < 32 reads row rr = lane & 31, chunk 2j + grp:
     //   rr * ROW_A + 16 (grp + g(rr)) + 32 j.
     // Region B (last 128 B of each row): rows of 128 B, chunk c of row r at
@@ -380,6 +382,7 @@ hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream)
 }
 
 template hipError_t launch_decode_wide<4, 3>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide<4, 4>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<4, 2>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<2, 3>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<2, 2>(const DecodeParams&, hipStream_t);

@@ -81,6 +81,7 @@ BF16_CASES = [
     (100, None), (16, {"heads_per_group": 16, "variant": 1}),
     # wide-wave kernels (32 heads per wave)
     (128, {"heads_per_group": 128, "variant": 3}), (128, {"heads_per_group": 128, "variant": 4}),
+    (128, {"heads_per_group": 128, "variant": 5}),
     (100, {"heads_per_group": 128, "variant": 3}), (64, {"heads_per_group": 64, "variant": 5}),
     (64, {"heads_per_group": 64, "variant": 6}), (32, {"heads_per_group": 32, "variant": 4}),
     (20, {"heads_per_group": 32, "variant": 4}),
