@@ -144,6 +144,118 @@ def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None):
                       "latent-form decode -> absorb_o, %.1f s" % (n, w.b, w.h, lens[0], dt)}
 
 
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o trace -- "
+             "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o fetch -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o write -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o cfetch -- "
+              "python3 bench.py --calibrate-copy 256",
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o cwrite -- "
+              "python3 bench.py --calibrate-copy 256",
+}
+
+
+def summarize_profiles(dirs, workload="dsv3_decode_b64_h128_T4096"):
+    """Turn the five rocprofv3 runs of PROFILE_CMDS (output directories in that
+    order) into the committed summaries: profiles/<kernel>_<workload>.md and
+    the traffic figures bench.py reports (profiles/decode_traffic.json).
+    Pure file processing, no GPU."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+        if not files:
+            raise SystemExit("no *%s under %s" % (suffix, d))
+        with open(files[0], newline="") as f:
+            return list(csv.DictReader(f))
+
+    def counter_means(d):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])  # sum over XCD/SE instances
+        per = {}
+        for (name, _), v in acc.items():
+            per.setdefault(name, []).append(v)
+        return {n: sum(v) / len(v) for n, v in per.items()}
+
+    stats = rows(dirs[0], "kernel_stats.csv")
+    fetch, write = counter_means(dirs[1]), counter_means(dirs[2])
+    cfetch, cwrite = counter_means(dirs[3]), counter_means(dirs[4])
+    copy_kib = 256 * 1024.0
+    cf = max((v for n, v in cfetch.items() if "copy" in n.lower()), default=None)
+    cw = max((v for n, v in cwrite.items() if "copy" in n.lower()), default=None)
+    if cf is None or cw is None:
+        raise SystemExit("no copy kernel in the calibration runs")
+    fs, ws_ = copy_kib / cf, copy_kib / cw
+    dec = [n for n in fetch if "decode_" in n and "_kernel" in n]
+    if len(dec) != 1:
+        raise SystemExit("expected one attention kernel in the counter runs, got %s" % dec)
+    dname = dec[0]
+    import re
+    short = re.search(r"decode_\w+(<[^>]*>)?", dname).group(0)
+    family = short.split("<")[0]
+    hbm = int(round((fetch[dname] * fs + write[dname] * ws_) * 1024))
+    w = workloads_counts(workload)
+    traffic = {
+        "kernel": short, "kernel_source_sha": kernel_source_hash(), "workload": workload,
+        "hbm_bytes_per_launch": hbm, "fetch_kib_per_launch": round(fetch[dname], 1),
+        "write_kib_per_launch": round(write[dname], 1), "fetch_scale": round(fs, 4),
+        "write_scale": round(ws_, 4),
+        "calibration": "plain 256 MiB device copy (bench.py --calibrate-copy 256): FETCH_SIZE "
+                       "%.1f KiB, WRITE_SIZE %.1f KiB per copy" % (cf, cw)}
+    lines = ["# %s on %s (bf16, b=64, h=128, 4096 cached tokens)" % (short, workload), "",
+             "MI355X (gfx950), ROCm 7.2, one GPU.  Commands, run from the repository root with",
+             "`export TMPDIR=/tmp` (DIR: any output directory), then this summary:", "", "```"]
+    lines += [PROFILE_CMDS[k] for k in ("trace", "fetch", "write", "cfetch", "cwrite")]
+    lines += ["python3 bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR CFETCH_DIR CWRITE_DIR",
+              "```", "", "## Kernel trace (`*_kernel_stats.csv`), durations in microseconds", "",
+              "Calls include warm-up steps; `reduce_kernel` is the cache-evicting read of a",
+              "512 MiB buffer between steps (outside the timed region).", "",
+              "| kernel | calls | avg | min | max | % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        nm = r["Name"]
+        nm = nm if len(nm) <= 90 else nm[:87] + "..."
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            nm.replace("|", "/"), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines += ["", "## HBM traffic per dispatch (`FETCH_SIZE`, `WRITE_SIZE`, KiB; mean over dispatches)", "",
+              "Calibration: a plain 256 MiB device-to-device copy reads FETCH_SIZE %.1f KiB and" % cf,
+              "WRITE_SIZE %.1f KiB, so FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f to give bytes." % (cw, fs, ws_),
+              "", "| kernel | FETCH_SIZE | WRITE_SIZE | HBM MB (scaled) |", "|---|---|---|---|"]
+    for n in fetch:
+        if "mla355" not in n:
+            continue
+        nm = n if len(n) <= 90 else n[:87] + "..."
+        lines.append("| %s | %.1f | %.1f | %.1f |" % (nm, fetch[n], write.get(n, 0.0),
+                                                      (fetch[n] * fs + write.get(n, 0.0) * ws_) * 1024 / 1e6))
+    lines += ["", "Algorithmic bytes of one attention launch: %.1f MB (latent cache, queries," % (w / 1e6),
+              "outputs and lse).  Measured %.1f MB; the difference is mostly the split-KV" % (hbm / 1e6),
+              "partials (written here, read back by the combine kernel)."]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", "%s_%s.md" % (family, workload))
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print(md)
+    print(TRAFFIC_FILE)
+
+
+def workloads_counts(workload):
+    """Algorithmic bytes of one attention launch of a named workload."""
+    import workloads
+    for cfg in workloads.CONFIGS.values():
+        if cfg.name == workload and cfg.lengths == "fixed":
+            return work_counts(cfg.b, cfg.h, [cfg.t_max] * cfg.b)["decode"][1]
+    raise SystemExit("no fixed-length workload named %s" % workload)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,9 +272,16 @@ def main():
                          "the reference for scaling HBM traffic counters")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the hash of the attention kernel's sources and exit")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar="DIR",
+                    help="write the profile summaries under profiles/ from the output directories "
+                         "of the five rocprofv3 runs (trace, fetch, write, copy fetch, copy write) "
+                         "and exit (no GPU needed)")
     args = ap.parse_args()
     if args.print_source_hash:
         print(kernel_source_hash())
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
         return
 
     if args.gpus != 1:
