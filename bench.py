@@ -267,6 +267,9 @@ def main():
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--hpg", type=int, default=0, help="heads per workgroup (0 = auto)")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="read the cache through a paged pool of BLOCK-token blocks (shuffled "
+                         "block table) with mla_decode_paged")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and exit: "
                          "the reference for scaling HBM traffic counters")
@@ -322,6 +325,21 @@ def main():
     if args.variant:
         sched["variant"] = args.variant
     bufs = mla.alloc_step(w.b, w.h, w.t_max, w.dtype, config=sched or None)
+    pool = block_table = None
+    if args.paged:
+        # every row's cache rows scattered over a seeded random permutation of blocks
+        bs = args.paged
+        mb = -(-w.t_max // bs)
+        g = torch.Generator().manual_seed(4242)
+        perm = torch.randperm(w.b * mb, generator=g).reshape(w.b, mb)
+        pool = torch.zeros((w.b * mb, bs, D_QK), dtype=w.dtype, device=dev)
+        padded = torch.zeros((w.b, mb * bs, D_QK), dtype=w.dtype, device=dev)
+        padded[:, : w.t_max] = w.cache
+        pool[perm.reshape(-1).to(dev)] = padded.reshape(w.b * mb, bs, D_QK)
+        del padded
+        block_table = perm.to(torch.int32).to(dev)
+        need = mla.mla_decode_paged_workspace_bytes(w.b, w.h, pool.shape[0], bs, mb, sched or None)
+        bufs.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     # Cache eviction between steps: READ a 512 MiB buffer (more than the 4 MB
     # L2s plus the 256 MB Infinity Cache).  Reading leaves only clean lines
     # behind; overwriting the buffer instead would leave ~256 MB of dirty lines
@@ -340,8 +358,14 @@ def main():
         c = dict(sched)
         if i is not None:
             c["profile_events"] = (ev[i][1].value, ev[i][2].value)
-        mla.mla_step(q_nope, q_rope, w_uk, w_uv, w.cache, w.seqlens, w.scale, bufs,
-                     config=c or None)
+        if pool is None:
+            mla.mla_step(q_nope, q_rope, w_uk, w_uv, w.cache, w.seqlens, w.scale, bufs,
+                         config=c or None)
+        else:
+            mla.mla_absorb_q(q_nope, w_uk, q_rope, bufs.q_prime)
+            mla.mla_decode_paged(bufs.q_prime, pool, block_table, w.seqlens, w.scale, bufs.out,
+                                 bufs.lse, bufs.workspace, config=c or None)
+            mla.mla_absorb_o(bufs.out, w_uv, bufs.y)
 
     for _ in range(W):
         if flush is not None:
@@ -379,7 +403,7 @@ def main():
     value = step_flop / (ms * 1e-3) / 1e12
     k_gbs = dec_bytes / (kms * 1e-3) / 1e9
     k_tfl = dec_flop / (kms * 1e-3) / 1e12
-    traffic = load_traffic(cfg.name)
+    traffic = None if args.paged else load_traffic(cfg.name)
     log("step: mean %.2f us (min %.2f, max %.2f); split-KV kernel mean %.2f us (min %.2f); "
         "back-to-back step %.2f us; wall %.3f s for %d steps" %
         (ms * 1e3, min(step_ms) * 1e3, max(step_ms) * 1e3, kms * 1e3, min(kern_ms) * 1e3,
@@ -404,12 +428,15 @@ def main():
                    "sum_cached_tokens": int(sum(lens)), "d_latent": D_C, "d_rope": D_R,
                    "step": "absorb_q + decode (plan, split-KV, combine) + absorb_o",
                    "cache_evicted_between_steps": flush is not None,
-                   "schedule": sched or "auto"},
+                   "schedule": sched or "auto",
+                   "cache_layout": ("paged, %d-token blocks, shuffled block table" % args.paged
+                                    if args.paged else "contiguous")},
         "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_flop": step_flop,
         "step_bytes": step_bytes,
         "ms_per_step_back_to_back": round(b2b_ms, 5),
-        "roofline": {"kernel": mla.mla_decode_kernel_name(w.dtype, w.h, sched or None),
+        "roofline": {"kernel": (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
+                                else mla.mla_decode_kernel_name(w.dtype, w.h, sched or None)),
                      "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(kms * 1e3, 2),

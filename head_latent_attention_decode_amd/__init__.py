@@ -64,10 +64,22 @@ _lib.mla_decode_kernel_name.argtypes = [_ci, _ci, ctypes.POINTER(MLAConfig)]
 _lib.mla_decode_ex.restype = _ci
 _lib.mla_decode_ex.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
                                ctypes.POINTER(MLAConfig), _vp]
+_lib.mla_decode_paged_workspace_bytes.restype = _sz
+_lib.mla_decode_paged_workspace_bytes.argtypes = [_ci, _ci, _ci, _ci, _ci, _ci,
+                                                  ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_paged_kernel_name.restype = ctypes.c_char_p
+_lib.mla_decode_paged_kernel_name.argtypes = [_ci, _ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_paged.restype = _ci
+_lib.mla_decode_paged.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp, _vp,
+                                  _vp, _sz, _vp]
+_lib.mla_decode_paged_ex.restype = _ci
+_lib.mla_decode_paged_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp,
+                                     _vp, _vp, _sz, ctypes.POINTER(MLAConfig), _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
-                    "mla_decode_ex", "mla_decode_kernel_name")
+                    "mla_decode_ex", "mla_decode_kernel_name", "mla_decode_paged_workspace_bytes",
+                    "mla_decode_paged", "mla_decode_paged_ex", "mla_decode_paged_kernel_name")
 
 
 class MLAError(RuntimeError):
@@ -204,6 +216,59 @@ def mla_decode(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, works
     else:
         st = _lib.mla_decode_ex(_dtype_code(dt), b, h, t_max, *args, _cfg(config), _stream(stream))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_paged_kernel_name(h: int, config=None):
+    """Name of the attention kernel mla_decode_paged would launch (pure host); None if rejected."""
+    name = _lib.mla_decode_paged_kernel_name(MLA_DTYPE_BF16, h, _cfg(config))
+    return None if name is None else name.decode()
+
+
+def mla_decode_paged_workspace_bytes(b: int, h: int, num_blocks: int, block_size: int,
+                                     max_blocks: int, config=None) -> int:
+    """Bytes of workspace mla_decode_paged needs (pure host computation, no GPU)."""
+    return int(_lib.mla_decode_paged_workspace_bytes(MLA_DTYPE_BF16, b, h, num_blocks, block_size,
+                                                     max_blocks, _cfg(config)))
+
+
+def mla_decode_paged(q_prime, kv_pool, block_table, seqlens, softmax_scale, out=None, lse=None,
+                     workspace=None, config=None, stream=None):
+    """Latent-form MLA decode over a paged cache.  Returns (out [b,h,512], lse [b,h] fp32).
+
+    q_prime [b,h,576] bf16; kv_pool [num_blocks, block_size, 576] bf16; block_table
+    [b, max_blocks] int32 and seqlens [b] int32 on the GPU.  Token t of row i is row
+    t % block_size of block block_table[i, t // block_size].
+    """
+    b, h, _ = q_prime.shape
+    num_blocks, block_size, _ = kv_pool.shape
+    max_blocks = block_table.shape[1]
+    dev = q_prime.device
+    dt = torch.bfloat16
+    if out is None:
+        out = torch.empty((b, h, D_C), dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((b, h), dtype=torch.float32, device=dev)
+    need = mla_decode_paged_workspace_bytes(b, h, num_blocks, block_size, max_blocks, config)
+    if need == 0:
+        raise ValueError("invalid paged decode problem or config: b=%d h=%d blocks=%d x %d, "
+                         "max_blocks=%d" % (b, h, num_blocks, block_size, max_blocks))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    args = (_dev(q_prime, "q_prime", (b, h, D_QK), dt),
+            _dev(kv_pool, "kv_pool", (num_blocks, block_size, D_QK), dt),
+            ctypes.c_int(num_blocks), ctypes.c_int(block_size),
+            _dev(block_table, "block_table", (b, max_blocks), torch.int32), ctypes.c_int(max_blocks),
+            _dev(seqlens, "seqlens", (b,), torch.int32), ctypes.c_float(float(softmax_scale)),
+            _dev(out, "out", (b, h, D_C), dt), _dev(lse, "lse", (b, h), torch.float32),
+            ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()))
+    if config is None:
+        st = _lib.mla_decode_paged(MLA_DTYPE_BF16, b, h, *args, _stream(stream))
+    else:
+        st = _lib.mla_decode_paged_ex(MLA_DTYPE_BF16, b, h, *args, _cfg(config), _stream(stream))
+    _check(st, "mla_decode_paged")
     return out, lse
 
 

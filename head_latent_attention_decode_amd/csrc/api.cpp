@@ -74,6 +74,32 @@ mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* c
     return MLA_OK;
 }
 
+// Schedule for a paged cache: only the wide-wave kernels address the block
+// pool, so the automatic choice is the wide kernel with the fewest heads per
+// group that covers h (32, 64 or 128), and an explicit choice must be one.
+mla_status_t choose_paged_schedule(int h, const mla_decode_config_t* cfg, Schedule* s)
+{
+    mla_decode_config_t c{};
+    if (cfg) c = *cfg;
+    if (c.heads_per_group == 0) c.heads_per_group = h <= 32 ? 32 : h <= 64 ? 64 : 128;
+    if (c.variant == 0) c.variant = c.heads_per_group == 64 ? 6 : 4;
+    const mla_status_t st = choose_schedule(MLA_DTYPE_BF16, h, &c, s);
+    if (st != MLA_OK) return st;
+    if (!bf16_variant_pages(s->hpg, s->variant)) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+bool paged_dims_ok(int b, int h, int num_blocks, int block_size, int max_blocks)
+{
+    if (b <= 0 || h <= 0 || num_blocks <= 0 || block_size <= 0 || max_blocks <= 0) return false;
+    if (block_size % 32 != 0) return false;
+    const int64_t t_max = (int64_t)max_blocks * block_size;
+    // the plan covers lengths rounded up to whole 32-token tiles
+    if ((int64_t)b * (t_max + 32) >= ((int64_t)1 << 31)) return false;
+    if ((int64_t)b * (int64_t)h >= ((int64_t)1 << 31) / kDqk) return false;
+    return true;
+}
+
 bool dims_ok(int b, int h, int t_max)
 {
     if (b <= 0 || h <= 0 || t_max < 0) return false;
@@ -119,7 +145,7 @@ const char* mla_decode_kernel_name(mla_dtype_t dt, int h, const mla_decode_confi
     Schedule s;
     if (choose_schedule(dt, h, cfg, &s) != MLA_OK) return nullptr;
     if (dt == MLA_DTYPE_F32) return "decode_f32_kernel";
-    return bf16_kernel_name(s.hpg, s.variant);
+    return bf16_kernel_name(s.hpg, s.variant, false);
 }
 
 size_t mla_decode_workspace_bytes(mla_dtype_t dt, int b, int h, int t_max)
@@ -155,6 +181,9 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     p.lse = lse;
     p.plse = (float*)(ws + w.plse_off);
     p.po = (void*)(ws + w.po_off);
+    p.block_table = nullptr;
+    p.seqlens = seqlens;
+    p.num_blocks = p.block_size = p.max_blocks = 0;
     p.b = b;
     p.h = h;
     p.t_max = t_max;
@@ -164,7 +193,7 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
 
     hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
     hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, plan,
+    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, 1, plan,
                                dt == MLA_DTYPE_BF16, out, lse, hs);
     if (e != hipSuccess) return MLA_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
@@ -184,6 +213,94 @@ mla_status_t mla_decode(mla_dtype_t dt, int b, int h, int t_max, const void* q_p
 {
     return mla_decode_ex(dt, b, h, t_max, q_prime, cache, seqlens, softmax_scale, out, lse,
                          workspace, workspace_bytes, nullptr, stream);
+}
+
+size_t mla_decode_paged_workspace_bytes(mla_dtype_t dt, int b, int h, int num_blocks,
+                                        int block_size, int max_blocks,
+                                        const mla_decode_config_t* cfg)
+{
+    if (dt != MLA_DTYPE_BF16 || !paged_dims_ok(b, h, num_blocks, block_size, max_blocks)) return 0;
+    Schedule s;
+    if (choose_paged_schedule(h, cfg, &s) != MLA_OK) return 0;
+    return workspace_layout(b, h, s.n_chunks, 2).total;
+}
+
+const char* mla_decode_paged_kernel_name(mla_dtype_t dt, int h, const mla_decode_config_t* cfg)
+{
+    if (dt != MLA_DTYPE_BF16 || h <= 0) return nullptr;
+    Schedule s;
+    if (choose_paged_schedule(h, cfg, &s) != MLA_OK) return nullptr;
+    return bf16_kernel_name(s.hpg, s.variant, true);
+}
+
+mla_status_t mla_decode_paged_ex(mla_dtype_t dt, int b, int h, const void* q_prime,
+                                 const void* kv_pool, int num_blocks, int block_size,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* seqlens, float softmax_scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 const mla_decode_config_t* cfg, void* stream)
+{
+    if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
+    if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+    if (!paged_dims_ok(b, h, num_blocks, block_size, max_blocks)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!q_prime || !kv_pool || !block_table || !seqlens || !out || !lse || !workspace)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_prime) || !aligned16(kv_pool) || !aligned16(block_table) ||
+        !aligned16(seqlens) || !aligned16(out) || !aligned16(lse) ||
+        ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    Schedule s;
+    const mla_status_t st = choose_paged_schedule(h, cfg, &s);
+    if (st != MLA_OK) return st;
+    const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks, 2);
+    if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    const int t_max = max_blocks * block_size;
+
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    int32_t* plan = (int32_t*)ws;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = kv_pool;
+    p.plan = plan;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (void*)(ws + w.po_off);
+    p.block_table = block_table;
+    p.seqlens = seqlens;
+    p.num_blocks = num_blocks;
+    p.block_size = block_size;
+    p.max_blocks = max_blocks;
+    p.b = b;
+    p.h = h;
+    p.t_max = t_max;
+    p.n_chunks = s.n_chunks;
+    p.n_hg = s.n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
+    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
+    // tile-aligned plan: every segment starts at a multiple of 32 tokens
+    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, 32, 32, plan, true, out, lse, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
+    e = launch_decode_bf16(p, s.hpg, s.variant, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
+    e = launch_combine(true, plan, b, h, p.plse, p.po, out, lse, hs);
+    return hip_status(e);
+}
+
+mla_status_t mla_decode_paged(mla_dtype_t dt, int b, int h, const void* q_prime, const void* kv_pool,
+                              int num_blocks, int block_size, const int32_t* block_table,
+                              int max_blocks, const int32_t* seqlens, float softmax_scale, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return mla_decode_paged_ex(dt, b, h, q_prime, kv_pool, num_blocks, block_size, block_table,
+                               max_blocks, seqlens, softmax_scale, out, lse, workspace,
+                               workspace_bytes, nullptr, stream);
 }
 
 mla_status_t mla_absorb_q(mla_dtype_t dt, int b, int h, const void* q_nope, const void* w_uk,

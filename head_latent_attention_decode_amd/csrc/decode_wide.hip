@@ -68,7 +68,11 @@ struct WideTiling {
     static_assert(LOADS <= KS, "refill spread over the score steps");
 };
 
-template <int NW, int STAGES>
+// Scalar (constant address space) view of device data that no kernel writes
+// while this one runs: a uniform index loads through the scalar cache.
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+
+template <int NW, int STAGES, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
 {
     using T = WideTiling<NW, STAGES>;
@@ -138,23 +142,50 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
         const int row_hi = plan_at(pv.cu() + r + 1);
         const int seg_end = min(end, row_hi);
         const int seg_a = pos - row_lo;
-        const int seg_len = seg_end - pos;
+        int seg_len = seg_end - pos;
+        if (PAGED) {
+            // the plan covers lengths rounded up to whole tiles: mask the rest
+            const int L = min(max(plan_at(p.seqlens + r), 0), p.t_max);
+            seg_len = max(0, min(seg_len, L - seg_a));
+        }
         const int split_j = k - row_lo / chunk;
         const bool final_out = plan_at(pv.nsplit() + r) == 1;
         const int slot = plan_at(pv.base() + r) + split_j;
         const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
         const int n_tiles = (seg_len + T::N - 1) / T::N;
 
+        // Global address of the first row of `tile`.  Paged: tiles are issued
+        // once each, in increasing order, so the block-table position of the
+        // next one is tracked (segments start at multiples of the tile, and
+        // the block size is a multiple of it: a tile never straddles blocks).
+        int pg_blk = 0, pg_off = 0;
+        if (PAGED) {
+            pg_blk = seg_a / p.block_size;
+            pg_off = seg_a - pg_blk * p.block_size;
+        }
+        auto tile_ptr = [&](int tile) -> const unsigned char* {
+            if (!PAGED) return seg_base + (size_t)tile * T::N * kRowBytesBf16;
+            // a scalar load: its wait does not queue behind the tile DMAs in flight
+            const int e = min(max(*(cint32_t*)(p.block_table + (size_t)r * p.max_blocks + pg_blk), 0),
+                              p.num_blocks - 1);
+            const unsigned char* a = cg + ((size_t)e * p.block_size + pg_off) * kRowBytesBf16;
+            pg_off += T::N;
+            if (pg_off == p.block_size) {
+                pg_off = 0;
+                ++pg_blk;
+            }
+            return a;
+        };
+
         // DMA instruction `li` (0 .. LOADS-1) of this wave's share of `tile`
-        // into stage SC.  Rows past the segment end re-read its last row (the
-        // scores of those slots are masked), so every access stays inside the
-        // rows of this segment.
-        auto issue_load = [&](auto SC, int tile, int li) {
+        // (first row at tptr) into stage SC.  Rows past the segment end
+        // re-read its last row (the scores of those slots are masked), so
+        // every access stays inside the rows of this segment.
+        auto issue_load = [&](auto SC, const unsigned char* tptr, int tile, int li) {
             const int t0 = tile * T::N;
             const int last = min(T::N, seg_len - t0) - 1;
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(seg_base + (size_t)t0 * kRowBytesBf16), (short)0,
-                (last + 1) * kRowBytesBf16, kBufferFlags);
+                (void*)tptr, (short)0, (last + 1) * kRowBytesBf16, kBufferFlags);
             lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
             if (li < T::LOADS_A) {
                 const int row = wave + li * NW;
@@ -174,8 +205,9 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             }
         };
         auto issue_tile = [&](auto SC, int tile) {
+            const unsigned char* tp = tile_ptr(tile);
 #pragma unroll
-            for (int li = 0; li < T::LOADS; ++li) issue_load(SC, tile, li);
+            for (int li = 0; li < T::LOADS; ++li) issue_load(SC, tp, tile, li);
         };
         // Wait until this wave's share of tile t has landed.  Tile 0 goes out
         // before the queries, tiles 1 .. STAGES-2 right after them, and step i
@@ -234,9 +266,11 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             constexpr int S = decltype(SC)::value;
             constexpr int SR = (S + STAGES - 1) % STAGES;  // stage of tile i-1 = refill target
             lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
+            const bool refill = i + STAGES - 1 < n_tiles;
+            // the refill's address first: a paged lookup completes during the barrier
+            const unsigned char* rptr = refill ? tile_ptr(i + STAGES - 1) : nullptr;
             wait_tile(i);
             lds_exchange_barrier();  // tile i visible to all; everyone is done with tile i-1
-            const bool refill = i + STAGES - 1 < n_tiles;
 
             // ---- scores: S^T = K . Q'^T, refill DMA spread over the first steps
             // (two copies of the loop, with and without the refill, so that no
@@ -253,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
                     const bf16x8_t kf = kring[j % PF];
                     if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
                     sacc = (j == 0) ? M::mma(kf, qf[j], (acc_t){}) : M::mma(kf, qf[j], sacc);
-                    if (REFILL && j < T::LOADS) issue_load(IC<SR>{}, i + STAGES - 1, j);
+                    if (REFILL && j < T::LOADS) issue_load(IC<SR>{}, rptr, i + STAGES - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
@@ -377,7 +411,10 @@ hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream)
 {
     using T = WideTiling<NW, STAGES>;
     const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
-    decode_wide_kernel<NW, STAGES><<<grid, T::THREADS, 0, stream>>>(p);
+    if (p.block_table != nullptr)
+        decode_wide_kernel<NW, STAGES, true><<<grid, T::THREADS, 0, stream>>>(p);
+    else
+        decode_wide_kernel<NW, STAGES, false><<<grid, T::THREADS, 0, stream>>>(p);
     return hipGetLastError();
 }
 

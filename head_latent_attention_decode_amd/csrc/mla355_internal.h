@@ -73,6 +73,14 @@ struct DecodeParams {
     float* lse;           // [b,h]
     float* plse;          // [slots,h]
     void* po;             // [slots,h,512] normalised partial outputs, dtype of the call
+    // paged cache (block_table != nullptr): cache is the block pool
+    // [num_blocks, block_size, 576]; row r's token t sits in block
+    // block_table[r * max_blocks + t / block_size] (clamped to the pool) at
+    // row t % block_size; t_max = max_blocks * block_size; the plan is
+    // tile-aligned and seqlens gives the true lengths.
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    int num_blocks, block_size, max_blocks;
     int b, h, t_max;
     int n_chunks;         // chunks per head group
     int n_hg;             // head groups
@@ -81,9 +89,10 @@ struct DecodeParams {
 
 // Launchers (return hipGetLastError() after the launch).
 // launch_plan also writes out = 0, lse = -inf for every row with no tokens
-// (no decode workgroup touches such a row).
+// (no decode workgroup touches such a row).  align > 1 lays the plan over
+// lengths (and a chunk) rounded up to multiples of align (paged cache).
 hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
-                       int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream);
+                       int align, int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream);
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream);
 
@@ -96,7 +105,8 @@ struct Bf16Variant {
 };
 bool bf16_variant_exists(int heads_per_group, int variant);
 int bf16_tile_tokens(int heads_per_group, int variant);
-const char* bf16_kernel_name(int heads_per_group, int variant);
+const char* bf16_kernel_name(int heads_per_group, int variant, bool paged);
+bool bf16_variant_pages(int heads_per_group, int variant);  // has a paged-cache form
 hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
                               hipStream_t stream);
 

@@ -37,13 +37,17 @@ __device__ int clamped_len(const int32_t* seqlens, int i, int t_max)
 
 // Workgroup 0, wave 0 builds the plan (two scans over the clamped lengths, 64
 // rows per step).  Workgroups 1.. give every row with no tokens out = 0 and
-// lse = -inf.
+// lse = -inf.  With align > 1 the plan is laid over the lengths rounded up to
+// a multiple of align, and the chunk too, so that every segment starts at a
+// multiple of align inside its row (the paged cache needs whole tiles inside
+// one block); the kernel masks the padding with the true lengths.
 template <typename OutT>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
                                                             int b, int h, int t_max, int n_chunks,
-                                                            int min_chunk, int32_t* plan,
+                                                            int min_chunk, int align, int32_t* plan,
                                                             OutT* out, float* lse)
 {
+    auto planned_len = [&](int i) { return (clamped_len(seqlens, i, t_max) + align - 1) / align * align; };
     const int tid = threadIdx.x;
     if (blockIdx.x > 0) {
         for (int r = blockIdx.x - 1; r < b; r += gridDim.x - 1) {
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (lane == 0) v.cu()[0] = 0;
     for (int base = 0; base < b; base += 64) {
         const int i = base + lane;
-        const int L = i < b ? clamped_len(seqlens, i, t_max) : 0;
+        const int L = i < b ? planned_len(i) : 0;
         const int inc = wave_inclusive_scan(L);
         if (i < b) v.cu()[i + 1] = carry + inc;
         carry += __shfl(inc, 63, 64);
@@ -71,6 +75,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int total = carry;
     int chunk = (int)(((long long)total + n_chunks - 1) / n_chunks);
     if (chunk < min_chunk) chunk = min_chunk;
+    chunk = (chunk + align - 1) / align * align;
     if (lane == 0) {
         plan[0] = total;
         plan[1] = chunk;
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     int slots = 0;
     for (int base = 0; base < b; base += 64) {
         const int i = base + lane;
-        const int L = i < b ? clamped_len(seqlens, i, t_max) : 0;
+        const int L = i < b ? planned_len(i) : 0;
         const int inc = wave_inclusive_scan(L);
         const int hi = carry + inc, lo = hi - L;
         int ns = 0, k_lo = 0, k_hi = 0;  // chunks k_lo .. k_hi-1 start inside row i
@@ -219,15 +224,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t*
 }  // namespace
 
 hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
-                       int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream)
+                       int align, int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream)
 {
     const unsigned grid = 1u + (unsigned)(b < kPlanMaxRowBlocks ? b : kPlanMaxRowBlocks);
     if (bf16)
         plan_kernel<__bf16><<<grid, kPlanThreads, 0, stream>>>(seqlens, b, h, t_max, n_chunks, min_chunk,
-                                                               plan, (__bf16*)out, lse);
+                                                               align, plan, (__bf16*)out, lse);
     else
         plan_kernel<float><<<grid, kPlanThreads, 0, stream>>>(seqlens, b, h, t_max, n_chunks, min_chunk,
-                                                              plan, (float*)out, lse);
+                                                              align, plan, (float*)out, lse);
     return hipGetLastError();
 }
 

@@ -147,11 +147,55 @@ mla_status_t mla_decode_ex(mla_dtype_t dtype, int b, int h, int t_max, const voi
  * mla_decode_kernel_name -- name of the split-KV attention kernel that
  * mla_decode_ex would launch for this dtype, head count and config (config
  * may be NULL: automatic), as profilers list it (for example
- * "decode_wide_kernel<4, 3>").  Pure host function: no HIP call, no GPU
+ * "decode_wide_kernel<4, 3, false>").  Pure host function: no HIP call, no GPU
  * needed.  The string is static and owned by the library.  Returns NULL for
  * an unknown dtype, h <= 0 or a config mla_decode_ex would reject.
  */
 const char* mla_decode_kernel_name(mla_dtype_t dtype, int h, const mla_decode_config_t* config);
+
+/*
+ * mla_decode_paged -- mla_decode over a paged latent cache.  The cached rows
+ * of every sequence live in fixed-size blocks of a shared pool, found through
+ * a block table (glossary, capacity and cost section: MLA leaves dynamic
+ * allocation to a paged scheme and the latent cache can still be split into
+ * blocks; relations section: such an allocator manages the physical latent
+ * blocks).  The operation on the rows is exactly mla_decode's.  For batch
+ * row i, cached token t (t < seqlens[i]) is row (t % block_size) of block
+ * block_table[i * max_blocks + t / block_size] of the pool.  Output, lse and
+ * the definition are those of mla_decode over the rows gathered that way.
+ * Layouts: q_prime [b,h,576] bf16; kv_pool [num_blocks, block_size, 576] bf16
+ * (row-major); block_table [b, max_blocks] int32 on the device; seqlens [b]
+ * int32 on the device, clamped to [0, max_blocks * block_size]; out
+ * [b,h,512] bf16 (written); lse [b,h] fp32 (written).  A block-table entry
+ * outside [0, num_blocks) is clamped into it (entries past a sequence's last
+ * block are never read).  block_size must be a positive multiple of 32 (a
+ * 32-token tile never straddles two blocks).
+ * workspace: device scratch of at least mla_decode_paged_workspace_bytes(...)
+ * bytes, 256-byte aligned, contents need not be initialised.
+ * Errors (host side, before any launch): MLA_ERR_UNSUPPORTED for dtype
+ * MLA_DTYPE_F32 or a config naming a kernel without a paged form;
+ * MLA_ERR_INVALID_ARGUMENT for a null or misaligned pointer, b, h,
+ * num_blocks, block_size or max_blocks <= 0, block_size not a multiple of 32,
+ * b * (max_blocks * block_size + 32) >= 2^31, or softmax_scale not finite or
+ * <= 0; MLA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t mla_decode_paged_workspace_bytes(mla_dtype_t dtype, int b, int h, int num_blocks,
+                                        int block_size, int max_blocks,
+                                        const mla_decode_config_t* config);
+mla_status_t mla_decode_paged(mla_dtype_t dtype, int b, int h, const void* q_prime,
+                              const void* kv_pool, int num_blocks, int block_size,
+                              const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_paged_ex(mla_dtype_t dtype, int b, int h, const void* q_prime,
+                                 const void* kv_pool, int num_blocks, int block_size,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* seqlens, float softmax_scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 const mla_decode_config_t* config, void* stream);
+/* Name of the attention kernel mla_decode_paged_ex would launch (pure host;
+ * NULL for a rejected dtype, h or config). */
+const char* mla_decode_paged_kernel_name(mla_dtype_t dtype, int h, const mla_decode_config_t* config);
 
 /*
  * mla_absorb_o -- output absorption.

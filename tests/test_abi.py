@@ -123,7 +123,7 @@ def test_python_binding_checks_tensors(mla):
 
 def test_decode_kernel_name_host_only(mla):
     # the schedule picks a kernel per head count; the query makes no HIP call
-    assert mla.mla_decode_kernel_name(torch.bfloat16, 128) == "decode_wide_kernel<4, 2>"
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 128) == "decode_wide_kernel<4, 2, false>"
     assert mla.mla_decode_kernel_name(torch.bfloat16, 16).startswith("decode_bf16_kernel<16,")
     assert mla.mla_decode_kernel_name(torch.float32, 16) == "decode_f32_kernel"
     assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"heads_per_group": 64, "variant": 3}) == \
@@ -132,3 +132,42 @@ def test_decode_kernel_name_host_only(mla):
     assert mla.mla_decode_kernel_name(torch.bfloat16, 0) is None
     assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"heads_per_group": 64, "variant": 4}) is None
     assert mla.mla_decode_kernel_name(torch.bfloat16, 64, {"variant": 99}) is None
+
+
+def _decode_paged(lib, dt=1, b=2, h=16, q=A, pool=A, nb=8, bs=64, bt=A, mb=4, sl=A, scale=SCALE,
+                  out=A, lse=A, ws=A, wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_decode_paged(dt, b, h, vp(q), vp(pool), nb, bs, vp(bt), mb, vp(sl),
+                                ctypes.c_float(scale), vp(out), vp(lse), vp(ws),
+                                ctypes.c_size_t(wsb), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dt": 0}, 2), ({"dt": 5}, 1), ({"bs": 48}, 1), ({"bs": 0}, 1), ({"bs": 16}, 1),
+    ({"nb": 0}, 1), ({"mb": 0}, 1), ({"b": 0}, 1), ({"h": 0}, 1), ({"bt": 0}, 1), ({"pool": 0}, 1),
+    ({"sl": 0}, 1), ({"pool": A + 8}, 1), ({"bt": A + 4}, 1), ({"ws": A + 64}, 1),
+    ({"scale": 0.0}, 1), ({"wsb": 1024}, 3), ({"b": 1 << 15, "mb": 1 << 10}, 1),
+])
+def test_decode_paged_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _decode_paged(lib, **kw) == status
+
+
+def test_decode_paged_host_queries(mla):
+    # only the wide kernels address a block pool; the query makes no HIP call
+    assert mla.mla_decode_paged_kernel_name(128) == "decode_wide_kernel<4, 2, true>"
+    assert mla.mla_decode_paged_kernel_name(100) == "decode_wide_kernel<4, 2, true>"
+    assert mla.mla_decode_paged_kernel_name(64) == "decode_wide_kernel<2, 2, true>"
+    assert mla.mla_decode_paged_kernel_name(16) == "decode_wide_kernel<1, 3, true>"
+    assert mla.mla_decode_paged_kernel_name(128, {"heads_per_group": 128, "variant": 3}) == \
+        "decode_wide_kernel<4, 3, true>"
+    assert mla.mla_decode_paged_kernel_name(16, {"heads_per_group": 16}) is None
+    assert mla.mla_decode_paged_kernel_name(64, {"heads_per_group": 64, "variant": 3}) is None
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    lib.mla_decode_paged_kernel_name.restype = ctypes.c_char_p
+    assert lib.mla_decode_paged_kernel_name(0, 16, None) is None  # fp32 has no paged form
+    # same workspace as the contiguous call of the same schedule
+    assert mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 64, 64) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
+    assert mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 48, 64) == 0
+    assert mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 64, 64, {"heads_per_group": 16}) == 0

@@ -196,6 +196,70 @@ def test_plan_bit_exact(mla, lens):
     assert got == ref
 
 
+# ---------------------------------------------------------------- paged latent cache
+
+def _paginate(w, block_size, seed, spare=3, unused_entry=None):
+    """Scatter every row's cache rows into randomly permuted blocks of a pool.
+    Spare blocks and the rows past each sequence end hold NaN (the cache tail
+    is NaN-poisoned), so a read of any row the method does not use shows up."""
+    b, t = w.b, w.t_max
+    mb = -(-t // block_size)
+    nb = b * mb + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(nb, generator=g)[: b * mb].reshape(b, mb)
+    padded = torch.full((b, mb * block_size, 576), float("nan"), dtype=w.cache.dtype, device="cuda")
+    padded[:, :t] = w.cache
+    pool = torch.full((nb, block_size, 576), float("nan"), dtype=w.cache.dtype, device="cuda")
+    pool[perm.reshape(-1).cuda()] = padded.reshape(b * mb, block_size, 576)
+    bt = perm.to(torch.int32)
+    if unused_entry is not None:
+        # entries past a sequence's last block are never read, whatever they hold
+        lens = w.seqlens.cpu().tolist()
+        for i, L in enumerate(lens):
+            bt[i, -(-max(L, 0) // block_size):] = unused_entry
+    return pool, bt.cuda()
+
+
+PAGED_CASES = [
+    (128, 64, None), (128, 32, None), (128, 256, None), (100, 64, None), (64, 64, None),
+    (16, 64, None), (20, 32, None),
+    (128, 64, {"heads_per_group": 128, "variant": 3}), (64, 128, {"heads_per_group": 64, "variant": 5}),
+]
+
+
+@pytest.mark.parametrize("h,bs,cfg", PAGED_CASES, ids=["h%d-bs%d-%s" % c for c in PAGED_CASES])
+def test_paged_edges_every_output(mla, h, bs, cfg):
+    w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=300 + h + bs, device="cuda")
+    pool, bt = _paginate(w, bs, seed=h + bs, unused_entry=-12345)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
+        c = dict(cfg or {})
+        c.update(extra)
+        out, lse = mla.mla_decode_paged(w.q_prime, pool, bt, w.seqlens, w.scale, config=c or None)
+        torch.cuda.synchronize()
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
+        assert torch.all(out[EDGE_LENS.index(0)] == 0)
+        assert torch.all(torch.isneginf(lse[EDGE_LENS.index(0)]))
+
+
+def test_paged_clamps_block_entries_and_is_deterministic(mla):
+    # an out-of-range entry that is read is clamped into the pool: the result is
+    # the decode over the rows gathered with the clamped table
+    # t_max = 5 whole blocks and no poisoning: every pool row is finite
+    w = workloads.make_custom(3, 128, [300, 64, 129], t_max=320, seed=41, device="cuda",
+                              poison=False)
+    pool, bt = _paginate(w, 64, seed=5, spare=0)
+    nb = pool.shape[0]
+    bt[0, 1] = nb + 17   # -> block nb - 1
+    bt[2, 0] = -4        # -> block 0
+    bt_c = bt.clamp(0, nb - 1).long().cpu()
+    gathered = pool[bt_c.reshape(-1).cuda()].reshape(3, -1, 576)[:, : w.t_max].contiguous()
+    out, lse = mla.mla_decode_paged(w.q_prime, pool, bt, w.seqlens, w.scale)
+    out2, lse2 = mla.mla_decode_paged(w.q_prime, pool, bt, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    check_decode(w.q_prime, gathered, w.seqlens, w.scale, out, lse, range(3))
+
+
 # ---------------------------------------------------------------- absorbs, bf16
 
 @pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8)])
@@ -225,6 +289,16 @@ def _full(mla, cid, rows):
 
 def test_full_dsv3_decode_b64_h128_T4096(mla):
     _full(mla, 2, [0, 17, 42, 63])
+
+
+def test_full_dsv3_decode_paged_bs64(mla):
+    # the same configuration through a paged pool (64-token blocks, shuffled)
+    w = workloads.make(2, device="cuda")
+    pool, bt = _paginate(w, 64, seed=77)
+    out, lse = mla.mla_decode_paged(w.q_prime, pool, bt, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, [0, 17, 42, 63])
 
 
 def test_full_few_heads_b128_h16_T8192(mla):
