@@ -267,6 +267,9 @@ def main():
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--hpg", type=int, default=0, help="heads per workgroup (0 = auto)")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--fp8", action="store_true",
+                    help="quantise the cache to per-token e4m3 (outside the timed region) and "
+                         "decode it with mla_decode_fp8")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="read the cache through a paged pool of BLOCK-token blocks (shuffled "
                          "block table) with mla_decode_paged")
@@ -326,6 +329,14 @@ def main():
         sched["variant"] = args.variant
     bufs = mla.alloc_step(w.b, w.h, w.t_max, w.dtype, config=sched or None)
     pool = block_table = None
+    codes = scales = None
+    if args.fp8 and args.paged:
+        print("--fp8 and --paged cannot be combined", file=sys.stderr)
+        sys.exit(2)
+    if args.fp8:
+        codes, scales = mla.mla_quantize_cache_fp8(w.cache)
+        need = mla.mla_decode_fp8_workspace_bytes(w.b, w.h, w.t_max, sched or None)
+        bufs.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if args.paged:
         # every row's cache rows scattered over a seeded random permutation of blocks
         bs = args.paged
@@ -358,7 +369,12 @@ def main():
         c = dict(sched)
         if i is not None:
             c["profile_events"] = (ev[i][1].value, ev[i][2].value)
-        if pool is None:
+        if codes is not None:
+            mla.mla_absorb_q(q_nope, w_uk, q_rope, bufs.q_prime)
+            mla.mla_decode_fp8(bufs.q_prime, codes, scales, w.seqlens, w.scale, bufs.out, bufs.lse,
+                               bufs.workspace, config=c or None)
+            mla.mla_absorb_o(bufs.out, w_uv, bufs.y)
+        elif pool is None:
             mla.mla_step(q_nope, q_rope, w_uk, w_uv, w.cache, w.seqlens, w.scale, bufs,
                          config=c or None)
         else:
@@ -395,6 +411,10 @@ def main():
     b2b_ms = hip.elapsed_ms(b0, b1) / K
 
     cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize)
+    if args.fp8:
+        # the cache streams 576 code bytes + a 4-byte scale per token
+        f, _ = cnt["decode"]
+        cnt["decode"] = (f, int(sum(lens)) * (D_QK + 4) + w.b * w.h * (D_QK * 2 + D_C * 2 + 4))
     step_flop = sum(f for f, _ in cnt.values())
     step_bytes = sum(bb for _, bb in cnt.values())
     dec_flop, dec_bytes = cnt["decode"]
@@ -403,7 +423,7 @@ def main():
     value = step_flop / (ms * 1e-3) / 1e12
     k_gbs = dec_bytes / (kms * 1e-3) / 1e9
     k_tfl = dec_flop / (kms * 1e-3) / 1e12
-    traffic = None if args.paged else load_traffic(cfg.name)
+    traffic = None if (args.paged or args.fp8) else load_traffic(cfg.name)
     log("step: mean %.2f us (min %.2f, max %.2f); split-KV kernel mean %.2f us (min %.2f); "
         "back-to-back step %.2f us; wall %.3f s for %d steps" %
         (ms * 1e3, min(step_ms) * 1e3, max(step_ms) * 1e3, kms * 1e3, min(kern_ms) * 1e3,
@@ -430,12 +450,14 @@ def main():
                    "cache_evicted_between_steps": flush is not None,
                    "schedule": sched or "auto",
                    "cache_layout": ("paged, %d-token blocks, shuffled block table" % args.paged
-                                    if args.paged else "contiguous")},
+                                    if args.paged else "contiguous"),
+                   "cache_dtype": "e4m3 codes + fp32 per-token scale" if args.fp8 else str(w.dtype)},
         "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_flop": step_flop,
         "step_bytes": step_bytes,
         "ms_per_step_back_to_back": round(b2b_ms, 5),
         "roofline": {"kernel": (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
+                                else mla.mla_decode_fp8_kernel_name(w.h, sched or None) if args.fp8
                                 else mla.mla_decode_kernel_name(w.dtype, w.h, sched or None)),
                      "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),

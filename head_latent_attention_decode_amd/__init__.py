@@ -72,6 +72,17 @@ _lib.mla_decode_paged_kernel_name.argtypes = [_ci, _ci, ctypes.POINTER(MLAConfig
 _lib.mla_decode_paged.restype = _ci
 _lib.mla_decode_paged.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp, _vp,
                                   _vp, _sz, _vp]
+_lib.mla_quantize_cache_fp8.restype = _ci
+_lib.mla_quantize_cache_fp8.argtypes = [ctypes.c_longlong, _vp, _vp, _vp, _vp]
+_lib.mla_decode_fp8_workspace_bytes.restype = _sz
+_lib.mla_decode_fp8_workspace_bytes.argtypes = [_ci, _ci, _ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_fp8_kernel_name.restype = ctypes.c_char_p
+_lib.mla_decode_fp8_kernel_name.argtypes = [_ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_fp8.restype = _ci
+_lib.mla_decode_fp8.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
+_lib.mla_decode_fp8_ex.restype = _ci
+_lib.mla_decode_fp8_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
+                                   ctypes.POINTER(MLAConfig), _vp]
 _lib.mla_decode_paged_ex.restype = _ci
 _lib.mla_decode_paged_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp,
                                      _vp, _vp, _sz, ctypes.POINTER(MLAConfig), _vp]
@@ -79,7 +90,9 @@ _lib.mla_decode_paged_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
                     "mla_decode_ex", "mla_decode_kernel_name", "mla_decode_paged_workspace_bytes",
-                    "mla_decode_paged", "mla_decode_paged_ex", "mla_decode_paged_kernel_name")
+                    "mla_decode_paged", "mla_decode_paged_ex", "mla_decode_paged_kernel_name",
+                    "mla_quantize_cache_fp8", "mla_decode_fp8_workspace_bytes", "mla_decode_fp8",
+                    "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name")
 
 
 class MLAError(RuntimeError):
@@ -269,6 +282,68 @@ def mla_decode_paged(q_prime, kv_pool, block_table, seqlens, softmax_scale, out=
     else:
         st = _lib.mla_decode_paged_ex(MLA_DTYPE_BF16, b, h, *args, _cfg(config), _stream(stream))
     _check(st, "mla_decode_paged")
+    return out, lse
+
+
+def mla_quantize_cache_fp8(cache, codes=None, scale=None, stream=None):
+    """Per-token OCP e4m3 form of bf16 latent rows [..., 576] -> (codes uint8 [..., 576],
+    scale fp32 [...]), with row ~ e4m3(codes) * scale."""
+    if cache.dtype != torch.bfloat16 or cache.shape[-1] != D_QK:
+        raise TypeError("cache must be bf16 [..., 576]")
+    lead = tuple(cache.shape[:-1])
+    n = 1
+    for x in lead:
+        n *= x
+    if codes is None:
+        codes = torch.empty(lead + (D_QK,), dtype=torch.uint8, device=cache.device)
+    if scale is None:
+        scale = torch.empty(lead, dtype=torch.float32, device=cache.device)
+    args = (_dev(cache, "cache", lead + (D_QK,), torch.bfloat16),
+            _dev(codes, "codes", lead + (D_QK,), torch.uint8), _dev(scale, "scale", lead, torch.float32))
+    _check(_lib.mla_quantize_cache_fp8(n, *args, _stream(stream)), "mla_quantize_cache_fp8")
+    return codes, scale
+
+
+def mla_decode_fp8_kernel_name(h: int, config=None):
+    """Name of the attention kernel mla_decode_fp8 would launch (pure host); None if rejected."""
+    name = _lib.mla_decode_fp8_kernel_name(h, _cfg(config))
+    return None if name is None else name.decode()
+
+
+def mla_decode_fp8_workspace_bytes(b: int, h: int, t_max: int, config=None) -> int:
+    return int(_lib.mla_decode_fp8_workspace_bytes(b, h, t_max, _cfg(config)))
+
+
+def mla_decode_fp8(q_prime, cache_codes, cache_scale, seqlens, softmax_scale, out=None, lse=None,
+                   workspace=None, config=None, stream=None):
+    """Latent-form MLA decode over an fp8 cache.  Returns (out [b,h,512] bf16, lse [b,h] fp32).
+
+    q_prime [b,h,576] bf16; cache_codes [b,t_max,576] uint8 (OCP e4m3); cache_scale
+    [b,t_max] fp32; seqlens [b] int32 on the GPU.
+    """
+    b, h, _ = q_prime.shape
+    t_max = cache_codes.shape[1]
+    dev = q_prime.device
+    if out is None:
+        out = torch.empty((b, h, D_C), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((b, h), dtype=torch.float32, device=dev)
+    need = mla_decode_fp8_workspace_bytes(b, h, t_max, config)
+    if need == 0:
+        raise ValueError("invalid fp8 decode problem or config: b=%d h=%d t_max=%d" % (b, h, t_max))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    args = (_dev(q_prime, "q_prime", (b, h, D_QK), torch.bfloat16),
+            _dev(cache_codes, "cache_codes", (b, t_max, D_QK), torch.uint8),
+            _dev(cache_scale, "cache_scale", (b, t_max), torch.float32),
+            _dev(seqlens, "seqlens", (b,), torch.int32), ctypes.c_float(float(softmax_scale)),
+            _dev(out, "out", (b, h, D_C), torch.bfloat16), _dev(lse, "lse", (b, h), torch.float32),
+            ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()))
+    if config is None:
+        st = _lib.mla_decode_fp8(b, h, t_max, *args, _stream(stream))
+    else:
+        st = _lib.mla_decode_fp8_ex(b, h, t_max, *args, _cfg(config), _stream(stream))
+    _check(st, "mla_decode_fp8")
     return out, lse
 
 

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla355.so")
-SOURCES = ["api.cpp", "plan_combine.hip", "decode_bf16.hip", "decode_wide.hip", "decode_f32.hip", "absorb.hip"]
+SOURCES = ["api.cpp", "plan_combine.hip", "decode_bf16.hip", "decode_wide.hip", "decode_f32.hip", "absorb.hip",
+           "quantize.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code (hipcc's host pass

@@ -100,6 +100,20 @@ bool paged_dims_ok(int b, int h, int num_blocks, int block_size, int max_blocks)
     return true;
 }
 
+// Schedule for an fp8 cache: the 16-head two-wave kernel is the one with an
+// fp8 form (the regime where halving the bytes pays is few heads per group).
+mla_status_t choose_fp8_schedule(int h, const mla_decode_config_t* cfg, Schedule* s)
+{
+    mla_decode_config_t c{};
+    if (cfg) c = *cfg;
+    if (c.heads_per_group == 0) c.heads_per_group = 16;
+    if (c.variant == 0) c.variant = 1;
+    const mla_status_t st = choose_schedule(MLA_DTYPE_BF16, h, &c, s);
+    if (st != MLA_OK) return st;
+    if (!bf16_variant_fp8(s->hpg, s->variant)) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
 bool dims_ok(int b, int h, int t_max)
 {
     if (b <= 0 || h <= 0 || t_max < 0) return false;
@@ -182,6 +196,7 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     p.plse = (float*)(ws + w.plse_off);
     p.po = (void*)(ws + w.po_off);
     p.block_table = nullptr;
+    p.cache_scale = nullptr;
     p.seqlens = seqlens;
     p.num_blocks = p.block_size = p.max_blocks = 0;
     p.b = b;
@@ -269,6 +284,7 @@ mla_status_t mla_decode_paged_ex(mla_dtype_t dt, int b, int h, const void* q_pri
     p.plse = (float*)(ws + w.plse_off);
     p.po = (void*)(ws + w.po_off);
     p.block_table = block_table;
+    p.cache_scale = nullptr;
     p.seqlens = seqlens;
     p.num_blocks = num_blocks;
     p.block_size = block_size;
@@ -301,6 +317,95 @@ mla_status_t mla_decode_paged(mla_dtype_t dt, int b, int h, const void* q_prime,
     return mla_decode_paged_ex(dt, b, h, q_prime, kv_pool, num_blocks, block_size, block_table,
                                max_blocks, seqlens, softmax_scale, out, lse, workspace,
                                workspace_bytes, nullptr, stream);
+}
+
+mla_status_t mla_quantize_cache_fp8(long long n_rows, const void* x, void* codes, float* scale,
+                                    void* stream)
+{
+    if (n_rows <= 0 || n_rows > ((long long)1 << 37)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!x || !codes || !scale) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scale & 3u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_quantize_fp8(n_rows, x, codes, scale, (hipStream_t)stream));
+}
+
+size_t mla_decode_fp8_workspace_bytes(int b, int h, int t_max, const mla_decode_config_t* cfg)
+{
+    if (!dims_ok(b, h, t_max)) return 0;
+    Schedule s;
+    if (choose_fp8_schedule(h, cfg, &s) != MLA_OK) return 0;
+    return workspace_layout(b, h, s.n_chunks, 2).total;
+}
+
+const char* mla_decode_fp8_kernel_name(int h, const mla_decode_config_t* cfg)
+{
+    if (h <= 0) return nullptr;
+    Schedule s;
+    if (choose_fp8_schedule(h, cfg, &s) != MLA_OK) return nullptr;
+    return fp8_kernel_name(s.hpg, s.variant);
+}
+
+mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
+                               const float* cache_scale, const int32_t* seqlens, float softmax_scale,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               const mla_decode_config_t* cfg, void* stream)
+{
+    if (!dims_ok(b, h, t_max)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!q_prime || !cache_codes || !cache_scale || !seqlens || !out || !lse || !workspace)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_prime) || !aligned16(cache_codes) || ((uintptr_t)cache_scale & 3u) != 0 ||
+        !aligned16(seqlens) || !aligned16(out) || !aligned16(lse) ||
+        ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    Schedule s;
+    const mla_status_t st = choose_fp8_schedule(h, cfg, &s);
+    if (st != MLA_OK) return st;
+    const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks, 2);
+    if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    int32_t* plan = (int32_t*)ws;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = cache_codes;
+    p.plan = plan;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (void*)(ws + w.po_off);
+    p.block_table = nullptr;
+    p.cache_scale = cache_scale;
+    p.seqlens = seqlens;
+    p.num_blocks = p.block_size = p.max_blocks = 0;
+    p.b = b;
+    p.h = h;
+    p.t_max = t_max;
+    p.n_chunks = s.n_chunks;
+    p.n_hg = s.n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
+    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
+    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, 1, plan, true, out,
+                               lse, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
+    e = launch_decode_bf16(p, s.hpg, s.variant, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
+    e = launch_combine(true, plan, b, h, p.plse, p.po, out, lse, hs);
+    return hip_status(e);
+}
+
+mla_status_t mla_decode_fp8(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
+                            const float* cache_scale, const int32_t* seqlens, float softmax_scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream)
+{
+    return mla_decode_fp8_ex(b, h, t_max, q_prime, cache_codes, cache_scale, seqlens, softmax_scale,
+                             out, lse, workspace, workspace_bytes, nullptr, stream);
 }
 
 mla_status_t mla_absorb_q(mla_dtype_t dt, int b, int h, const void* q_nope, const void* w_uk,

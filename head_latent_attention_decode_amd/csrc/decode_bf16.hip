@@ -60,6 +60,11 @@ struct Tiling {
     static constexpr int MBLK = kDc / WH;          // O^T blocks (WH latent columns each)
     static constexpr int SBLK = NT / WH;           // S^T blocks per wave per tile
     static constexpr int MERGE_FLOATS = MBLK * Mfma<WH>::kAcc + 2;  // per lane
+    // fp8 cache: a stage holds the tile's raw rows (576 B each) and per-token
+    // scales; the conversion pass writes the bf16 tile above into one buffer
+    static constexpr int ROW8 = kDqk;                      // fp8 row bytes
+    static constexpr int STG8_BYTES = N * ROW8 + N * 4;
+    static constexpr int DMA8 = N * ROW8 / 1024 / NW;      // 1 KB DMA instructions per wave
     static_assert(N % NW == 0, "region A rows split evenly over waves");
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
     static_assert(STAGES == 2 || GROUPS_B % NW == 0, "exact vmcnt accounting needs even B split");
@@ -69,10 +74,15 @@ struct Tiling {
     static_assert(TS == 1 || (TS - 1) * HS * 64 * MERGE_FLOATS * 4 <= TILE_BYTES, "merge area");
 };
 
-template <int WH, int HS, int TS, int NT, int STAGES>
+template <int WH, int HS, int TS, int NT, int STAGES, bool FP8>
 __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams p)
 {
     using T = Tiling<WH, HS, TS, NT, STAGES>;
+    static_assert(!FP8 || (STAGES == 2 && (T::N * T::ROW8) % (1024 * T::NW) == 0 && T::N <= 64 &&
+                           WH == 16 && NT % 16 == 0),
+                  "fp8 staging: two stages, whole DMA blocks per wave, one scale instruction, "
+                  "16-head waves over whole 16-row swizzle periods");
+    static_assert(!FP8 || STAGES * T::STG8_BYTES + T::TILE_BYTES <= 160 * 1024, "fp8 LDS budget");
     using M = Mfma<WH>;
     typedef typename M::acc_t acc_t;
 
@@ -153,7 +163,8 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
         const int split_j = k - row_lo / chunk;
         const bool final_out = pv.nsplit()[r] == 1;
         const int slot = pv.base()[r] + split_j;
-        const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
+        const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * (FP8 ? T::ROW8 : kRowBytesBf16);
+        const float* seg_scale = FP8 ? p.cache_scale + (size_t)r * p.t_max + seg_a : nullptr;
         const int n_tiles = (seg_len + T::N - 1) / T::N;
 
         // Queries: B operand of S^T = K . Q^T.  Lane -> head hl, k-slots
@@ -170,7 +181,37 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             }
         }
 
+        // fp8: the tile's rows are one contiguous run of N*576 bytes, copied
+        // as 1 KB blocks.  The buffer resource spans the valid rows only, and
+        // the whole offset is in the bounds-checked per-lane part, so a piece
+        // past the segment end reads as zero codes (finite; those tokens are
+        // masked).  Wave 0 also copies the N scales, 4 bytes per lane (past
+        // the valid rows they read as 0 the same way).
+        auto issue_tile8 = [&](auto SC, int tile) {
+            const int t0 = tile * T::N;
+            const int last = min(T::N, seg_len - t0) - 1;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(seg_base + (size_t)t0 * T::ROW8), (short)0, (last + 1) * T::ROW8, kBufferFlags);
+            lds_byte* st = stage_lds<T::STG8_BYTES, decltype(SC)::value>();
+#pragma unroll
+            for (int j = 0; j < T::DMA8; ++j) {
+                const int blk = wave * T::DMA8 + j;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(st + blk * 1024), 16,
+                                                         (unsigned)(blk * 1024 + lane * 16), 0, 0, 0);
+            }
+            if (wave == 0 && lane < T::N) {  // one 4-byte scale per lane
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(seg_scale + t0), (short)0, (last + 1) * 4, kBufferFlags);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::N * T::ROW8), 4,
+                                                         (unsigned)(lane * 4), 0, 0, 0);
+            }
+        };
+
         auto issue_tile = [&](auto SC, int tile) {
+            if (FP8) {
+                issue_tile8(SC, tile);
+                return;
+            }
             const int t0 = tile * T::N;
             const int last = min(T::N, seg_len - t0) - 1;  // last valid tile row
             // Buffer resource over this tile's valid rows.  Rows past the end of
@@ -227,7 +268,41 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             lds_exchange_barrier();
             if (it + STAGES - 1 < n_tiles) issue_tile(IC<(S + STAGES - 1) % STAGES>{}, it + STAGES - 1);
 
-            lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
+            // fp8: each wave converts the staged codes of its own NT token rows
+            // (the only rows its score and weighted-sum reads touch) into the
+            // bf16 tile, in the layout and swizzles of a DMA'd bf16 tile (e4m3
+            // values are exact in bf16; each token's scale is applied to its
+            // score and probability below).  Region A: lane = 8-code chunk of
+            // row tok0 + k (the row swizzle depends on k only, since tok0 is a
+            // multiple of 16); region B: 8 chunks x 8 rows per step.
+            lds_byte* tb = FP8 ? stage_lds<T::TILE_BYTES, 8>() : stage_lds<T::TILE_BYTES, S>();
+            const lds_byte* sg = stage_lds<T::STG8_BYTES, S>();
+            if (FP8) {
+                auto cvt8 = [](unsigned long long codes) -> bf16x8_t {
+                    const unsigned lo = (unsigned)codes, hi = (unsigned)(codes >> 32);
+                    const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+                    const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+                    const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+                    const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+                    return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+                };
+                const lds_byte* srcA = sg + tok0 * T::ROW8 + lane * 8;
+                lds_byte* dstA = tb + tok0 * 1024;
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const unsigned long long codes = *(const LDS_AS unsigned long long*)(srcA + k * T::ROW8);
+                    *(LDS_AS bf16x8_t*)(dstA + k * 1024 + ((lane ^ M::xa(k & 15)) << 4)) = cvt8(codes);
+                }
+                const int cb = lane & 7;
+#pragma unroll
+                for (int j = 0; j < NT / 8; ++j) {
+                    const int k = (lane >> 3) + 8 * j;
+                    const unsigned long long codes =
+                        *(const LDS_AS unsigned long long*)(sg + (tok0 + k) * T::ROW8 + kDc + cb * 8);
+                    *(LDS_AS bf16x8_t*)(tb + T::A_BYTES + (tok0 + k) * 128 + ((cb ^ xb(k & 15)) << 4)) = cvt8(codes);
+                }
+                lds_wave_sync();  // this wave's converted rows written before it reads them
+            }
             const int tvalid = seg_len - it * T::N - tok0;  // valid tokens for this wave (may be <= 0)
 
             // ---- S^T = K . Q^T -------------------------------------------------
@@ -265,12 +340,22 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             // sfin[sb][i] is the score of token tok0 + sb*WH + toff(i), head hl.
             float tmax = -INFINITY;
             const bool full = tvalid >= NT;
+            // fp8: per-token scale of every accumulator entry's token
+            float tsc[T::SBLK][M::kAcc];
+#pragma unroll
+            for (int sb = 0; sb < T::SBLK; ++sb)
+#pragma unroll
+                for (int i = 0; i < M::kAcc; ++i) {
+                    const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
+                    tsc[sb][i] = FP8 ? *(const LDS_AS float*)(sg + T::N * T::ROW8 + (tok0 + sb * WH + toff) * 4)
+                                     : 1.0f;
+                }
 #pragma unroll
             for (int sb = 0; sb < T::SBLK; ++sb) {
 #pragma unroll
                 for (int i = 0; i < M::kAcc; ++i) {
                     const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
-                    float v = sfin[sb][i] * p.scale_log2;
+                    float v = sfin[sb][i] * (FP8 ? p.scale_log2 * tsc[sb][i] : p.scale_log2);
                     if (!full && sb * WH + toff >= tvalid) v = -INFINITY;
                     sfin[sb][i] = v;
                     tmax = fmaxf(tmax, v);
@@ -297,10 +382,11 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
                 for (int i = 0; i < M::kAcc; ++i) {
                     const float e = exp2_fast(sfin[sb][i] - m_run);
                     l_run += e;
+                    const float pe = FP8 ? e * tsc[sb][i] : e;  // fp8: dequantising scale of V
                     if (WH == 16)
-                        pb[sb >> 1][(sb & 1) * 4 + i] = (__bf16)e;
+                        pb[sb >> 1][(sb & 1) * 4 + i] = (__bf16)pe;
                     else
-                        pb[sb * 2 + (i >> 3)][i & 7] = (__bf16)e;
+                        pb[sb * 2 + (i >> 3)][i & 7] = (__bf16)pe;
                 }
             }
 
@@ -351,7 +437,7 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             // subgroup merges them.  The merge area overlays the tile stages,
             // so first every wave must have finished reading the last tile.
             wg_barrier();
-            float* area = (float*)stage_lds<T::TILE_BYTES, 0>();
+            float* area = (float*)(FP8 ? stage_lds<T::TILE_BYTES, 8>() : stage_lds<T::TILE_BYTES, 0>());
             if (ts > 0) {
                 float* dst = area + ((size_t)((ts - 1) * HS + hs) * T::MERGE_FLOATS) * 64;
                 dst[lane] = m_run;
@@ -827,7 +913,17 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream)
 {
     using T = Tiling<WH, HS, TS, NT, STAGES>;
     const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
-    decode_bf16_kernel<WH, HS, TS, NT, STAGES><<<grid, T::THREADS, 0, stream>>>(p);
+    decode_bf16_kernel<WH, HS, TS, NT, STAGES, false><<<grid, T::THREADS, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+// fp8 latent cache (p.cache holds e4m3 codes, p.cache_scale per-token scales)
+template <int WH, int HS, int TS, int NT, int STAGES>
+hipError_t launch_variant_fp8(const DecodeParams& p, hipStream_t stream)
+{
+    using T = Tiling<WH, HS, TS, NT, STAGES>;
+    const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
+    decode_bf16_kernel<WH, HS, TS, NT, STAGES, true><<<grid, T::THREADS, 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -838,29 +934,45 @@ struct VariantEntry {
     hipError_t (*launch)(const DecodeParams&, hipStream_t);
     const char* name;        // kernel name as profilers print it
     const char* paged_name;  // the same for a paged cache; nullptr: not supported
+    hipError_t (*launch_fp8)(const DecodeParams&, hipStream_t);  // fp8 cache; nullptr: none
+    const char* fp8_name;
 };
 
-// heads_per_group, variant id, tile tokens, launcher, names
+// heads_per_group, variant id, tile tokens, launcher, names, fp8 launcher and name
 const VariantEntry kVariants[] = {
-    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2>", nullptr},
-    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>, "decode_bf16_kernel<16, 1, 1, 32, 2>", nullptr},
-    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>, "decode_bf16_kernel<16, 2, 2, 32, 2>", nullptr},
-    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>, "decode_bf16_kernel<32, 1, 1, 32, 2>", nullptr},
-    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>, "decode_bf16_kernel<16, 4, 1, 64, 2>", nullptr},
-    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>, "decode_bf16_kernel<32, 2, 1, 32, 4>", nullptr},
-    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>, "decode_bf16_kernel<32, 4, 1, 32, 4>", nullptr},
-    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>, "decode_bf16_kernel<16, 8, 1, 32, 2>", nullptr},
-    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>", nullptr},
+    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, false>", nullptr,
+     &launch_variant_fp8<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, true>"},
+    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>, "decode_bf16_kernel<16, 1, 1, 32, 2, false>", nullptr,
+     nullptr, nullptr},
+    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>, "decode_bf16_kernel<16, 2, 2, 32, 2, false>", nullptr,
+     nullptr, nullptr},
+    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>, "decode_bf16_kernel<32, 1, 1, 32, 2, false>", nullptr,
+     nullptr, nullptr},
+    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>, "decode_bf16_kernel<16, 4, 1, 64, 2, false>", nullptr,
+     nullptr, nullptr},
+    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>, "decode_bf16_kernel<32, 2, 1, 32, 4, false>", nullptr,
+     nullptr, nullptr},
+    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>, "decode_bf16_kernel<32, 4, 1, 32, 4, false>", nullptr,
+     nullptr, nullptr},
+    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>, "decode_bf16_kernel<16, 8, 1, 32, 2, false>", nullptr,
+     nullptr, nullptr},
+    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>", nullptr, nullptr, nullptr},
     // The three-stage ring (pair kernel <2, 3>) is switched off: it took a GPU
     // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
     // cause has not been found; every other variant passes the same tests.
-    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>", nullptr},
-    {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3, false>", "decode_wide_kernel<4, 3, true>"},
-    {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2, false>", "decode_wide_kernel<4, 2, true>"},
-    {128, 5, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4, false>", "decode_wide_kernel<4, 4, true>"},
-    {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3, false>", "decode_wide_kernel<2, 3, true>"},
-    {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2, false>", "decode_wide_kernel<2, 2, true>"},
-    {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3, false>", "decode_wide_kernel<1, 3, true>"},
+    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>", nullptr, nullptr, nullptr},
+    {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3, false>", "decode_wide_kernel<4, 3, true>",
+     nullptr, nullptr},
+    {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2, false>", "decode_wide_kernel<4, 2, true>",
+     nullptr, nullptr},
+    {128, 5, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4, false>", "decode_wide_kernel<4, 4, true>",
+     nullptr, nullptr},
+    {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3, false>", "decode_wide_kernel<2, 3, true>",
+     nullptr, nullptr},
+    {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2, false>", "decode_wide_kernel<2, 2, true>",
+     nullptr, nullptr},
+    {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3, false>", "decode_wide_kernel<1, 3, true>",
+     nullptr, nullptr},
 };
 
 const VariantEntry* find_variant(int hpg, int variant)
@@ -884,6 +996,18 @@ const char* bf16_kernel_name(int heads_per_group, int variant, bool paged)
     return v == nullptr ? nullptr : (paged ? v->paged_name : v->name);
 }
 
+bool bf16_variant_fp8(int heads_per_group, int variant)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    return v != nullptr && v->launch_fp8 != nullptr;
+}
+
+const char* fp8_kernel_name(int heads_per_group, int variant)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    return v == nullptr ? nullptr : v->fp8_name;
+}
+
 bool bf16_variant_pages(int heads_per_group, int variant)
 {
     const VariantEntry* v = find_variant(heads_per_group, variant);
@@ -901,6 +1025,10 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int va
 {
     const VariantEntry* v = find_variant(heads_per_group, variant);
     if (!v) return hipErrorInvalidValue;
+    if (p.cache_scale != nullptr) {
+        if (v->launch_fp8 == nullptr) return hipErrorInvalidValue;
+        return v->launch_fp8(p, stream);
+    }
     return v->launch(p, stream);
 }
 

@@ -80,6 +80,9 @@ struct DecodeParams {
     // tile-aligned and seqlens gives the true lengths.
     const int32_t* block_table;
     const int32_t* seqlens;
+    // fp8 cache (cache_scale != nullptr): cache holds OCP e4m3 codes
+    // [b, t_max, 576] and cache_scale [b, t_max] the per-token scales
+    const float* cache_scale;
     int num_blocks, block_size, max_blocks;
     int b, h, t_max;
     int n_chunks;         // chunks per head group
@@ -107,6 +110,9 @@ bool bf16_variant_exists(int heads_per_group, int variant);
 int bf16_tile_tokens(int heads_per_group, int variant);
 const char* bf16_kernel_name(int heads_per_group, int variant, bool paged);
 bool bf16_variant_pages(int heads_per_group, int variant);  // has a paged-cache form
+// fp8 latent cache: only some variants have a form that reads e4m3 codes
+bool bf16_variant_fp8(int heads_per_group, int variant);
+const char* fp8_kernel_name(int heads_per_group, int variant);
 hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
                               hipStream_t stream);
 
@@ -115,6 +121,9 @@ template <int NW, int STAGES>
 hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_quantize_fp8(long long n_rows, const void* x, void* codes, float* scale,
+                               hipStream_t stream);
 
 hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const void* w_uk,
                            const void* q_rope, void* q_prime, hipStream_t stream);

@@ -198,6 +198,57 @@ mla_status_t mla_decode_paged_ex(mla_dtype_t dtype, int b, int h, const void* q_
 const char* mla_decode_paged_kernel_name(mla_dtype_t dtype, int h, const mla_decode_config_t* config);
 
 /*
+ * mla_quantize_cache_fp8 -- per-token fp8 form of latent rows for
+ * mla_decode_fp8.  The pages define no quantised cache; this is the plainest
+ * form that keeps the scales out of the inner products.  For each row
+ * x[0:576] (bf16) of the n_rows rows:
+ *   scale    = max_i |x_i| / 448            (fp32, IEEE division; 448 is the
+ *                                           largest finite OCP e4m3 value)
+ *   codes[i] = e4m3(clamp(x_i / scale, -448, 448))   (fp32 quotient, rounded
+ *              to the nearest e4m3 value, ties to even; 0 when scale = 0)
+ * so that x_i ~ e4m3_value(codes[i]) * scale.  Codes are OCP FP8 E4M3 bytes
+ * (bias 7, no infinities, 0x7F/0xFF NaN).  Layouts: x [n_rows, 576] bf16,
+ * codes [n_rows, 576] uint8 (written), scale [n_rows] fp32 (written).
+ * A latent cache [b, t_max, 576] is n_rows = b * t_max rows.
+ * Errors: MLA_ERR_INVALID_ARGUMENT for n_rows <= 0 or > 2^37, a null pointer,
+ * x or codes not 16-byte aligned, or scale not 4-byte aligned.
+ */
+mla_status_t mla_quantize_cache_fp8(long long n_rows, const void* x, void* codes, float* scale,
+                                    void* stream);
+
+/*
+ * mla_decode_fp8 -- mla_decode over an fp8 latent cache: the same operation
+ * with each cached row replaced by its dequantised value
+ * e4m3_value(cache_codes[i, t, :]) * cache_scale[i, t] (the form written by
+ * mla_quantize_cache_fp8).  The cache streams at 580 bytes per token instead
+ * of 1152.  q_prime [b,h,576] bf16; cache_codes [b,t_max,576] uint8 (OCP e4m3);
+ * cache_scale [b,t_max] fp32; seqlens [b] int32 on the device (clamped to
+ * [0, t_max]); out [b,h,512] bf16 and lse [b,h] fp32 (written).  Scores and
+ * weighted sums run on bf16 MFMA with fp32 accumulation (e4m3 values are
+ * exact in bf16; each token's scale multiplies its score and probability).
+ * workspace: at least mla_decode_fp8_workspace_bytes(...) bytes, 256-byte
+ * aligned, contents need not be initialised.  config: as for mla_decode_ex;
+ * only the 16-heads-per-group kernel has an fp8 form (other choices give
+ * MLA_ERR_UNSUPPORTED).
+ * Errors (host side, before any launch): MLA_ERR_INVALID_ARGUMENT for a null
+ * or misaligned pointer (cache_scale: 4-byte alignment), b <= 0, h <= 0,
+ * t_max < 0, b*t_max >= 2^31, or softmax_scale not finite or <= 0;
+ * MLA_ERR_WORKSPACE_TOO_SMALL; MLA_ERR_UNSUPPORTED as above.
+ */
+size_t mla_decode_fp8_workspace_bytes(int b, int h, int t_max, const mla_decode_config_t* config);
+mla_status_t mla_decode_fp8(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
+                            const float* cache_scale, const int32_t* seqlens, float softmax_scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
+mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
+                               const float* cache_scale, const int32_t* seqlens, float softmax_scale,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               const mla_decode_config_t* config, void* stream);
+/* Name of the attention kernel mla_decode_fp8_ex would launch (pure host;
+ * NULL for a rejected h or config). */
+const char* mla_decode_fp8_kernel_name(int h, const mla_decode_config_t* config);
+
+/*
  * mla_absorb_o -- output absorption.
  *   y[b,h,:] = o[b,h,:] . W_UV[h]   (contracts d_c = 512)
  * Glossary, section on why decode absorbs: sum_t p_t (c_t W^UV_h) equals

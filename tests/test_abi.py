@@ -171,3 +171,30 @@ def test_decode_paged_host_queries(mla):
         mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
     assert mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 48, 64) == 0
     assert mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 64, 64, {"heads_per_group": 16}) == 0
+
+
+def test_fp8_validation_and_queries(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.mla_quantize_cache_fp8.argtypes = [ctypes.c_longlong, vp, vp, vp, vp]
+    assert lib.mla_quantize_cache_fp8(0, vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_quantize_cache_fp8(-5, vp(A), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_quantize_cache_fp8(10, vp(0), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_quantize_cache_fp8(10, vp(A + 8), vp(A), vp(A), vp(0)) == 1
+    assert lib.mla_quantize_cache_fp8(10, vp(A), vp(A), vp(A + 2), vp(0)) == 1
+    assert lib.mla_quantize_cache_fp8(1 << 40, vp(A), vp(A), vp(A), vp(0)) == 1
+
+    def dec(b=2, h=16, t=100, q=A, c=A, s=A, sl=A, scale=SCALE, out=A, lse=A, ws=A, wsb=1 << 30):
+        return lib.mla_decode_fp8(b, h, t, vp(q), vp(c), vp(s), vp(sl), ctypes.c_float(scale),
+                                  vp(out), vp(lse), vp(ws), ctypes.c_size_t(wsb), vp(0))
+    for kw, st in (({"q": 0}, 1), ({"c": 0}, 1), ({"s": 0}, 1), ({"s": A + 2}, 1), ({"c": A + 4}, 1),
+                   ({"b": 0}, 1), ({"t": -1}, 1), ({"scale": -1.0}, 1), ({"wsb": 100}, 3),
+                   ({"ws": A + 128}, 1), ({"b": 1 << 20, "t": 1 << 12}, 1)):
+        assert dec(**kw) == st, kw
+    # only the 16-heads-per-group kernel reads e4m3 codes
+    assert mla.mla_decode_fp8_kernel_name(16) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
+    assert mla.mla_decode_fp8_kernel_name(128) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
+    assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 128}) is None
+    assert mla.mla_decode_fp8_kernel_name(16, {"heads_per_group": 16, "variant": 2}) is None
+    assert mla.mla_decode_fp8_workspace_bytes(128, 16, 8192) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 128, 16, 8192)

@@ -260,6 +260,70 @@ def test_paged_clamps_block_entries_and_is_deterministic(mla):
     check_decode(w.q_prime, gathered, w.seqlens, w.scale, out, lse, range(3))
 
 
+# ---------------------------------------------------------------- fp8 latent cache
+
+def _fp8_from(w, poison=True):
+    """Quantise w's cache with the oracle's quantiser (test input); codes and
+    scales past each sequence end are NaN (0x7F, NaN scale) when poisoned."""
+    from oracle import fp8 as ofp8
+    lens = w.seqlens.cpu().tolist()
+    x = w.cache.float().cpu().numpy()
+    x = np.nan_to_num(x, nan=0.0)
+    codes, scale = ofp8.quantize_rows(x)
+    if poison:
+        for i, L in enumerate(lens):
+            codes[i, max(L, 0):] = 0x7F
+            scale[i, max(L, 0):] = np.nan
+    return (torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda(),
+            ofp8.dequantize(codes, np.nan_to_num(scale)))
+
+
+def test_fp8_quantiser_bit_exact(mla):
+    # integer codes decided in fp32 on both sides: compared exactly
+    from oracle import fp8 as ofp8
+    w = workloads.make_custom(3, 16, [700, 1, 333], seed=51, device="cuda", poison=False)
+    w.cache[1, 5] = 0.0                       # an all-zero row
+    w.cache[2, 7, 9] = -0.0
+    codes, scale = mla.mla_quantize_cache_fp8(w.cache)
+    torch.cuda.synchronize()
+    rc, rs = ofp8.quantize_rows(w.cache.float().cpu().numpy())
+    np.testing.assert_array_equal(scale.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+FP8_CASES = [16, 1, 3, 20, 128]
+
+
+@pytest.mark.parametrize("h", FP8_CASES, ids=["h%d" % h for h in FP8_CASES])
+def test_fp8_edges_every_output(mla, h):
+    w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=500 + h, device="cuda")
+    codes, scale, deq = _fp8_from(w)
+    ref_out, ref_lse = oracle.decode_latent(w.q_prime.cpu(), deq, w.seqlens.cpu(), w.scale)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
+        out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=extra or None)
+        torch.cuda.synchronize()
+        assert_out(to_np(out), ref_out, BF16_OUT_REL, "out %s" % extra)
+        assert_lse(to_np(lse), ref_lse, BF16_LSE_ABS)
+        assert torch.all(out[EDGE_LENS.index(0)] == 0)
+        assert torch.all(torch.isneginf(lse[EDGE_LENS.index(0)]))
+
+
+def test_full_few_heads_fp8_b128_h16_T8192(mla):
+    # the few-heads configuration with its cache quantised on the GPU; sampled
+    # rows against the oracle fed the same codes (decoded exactly)
+    from oracle import fp8 as ofp8
+    w = workloads.make(3, device="cuda", poison=False)
+    codes, scale = mla.mla_quantize_cache_fp8(w.cache)
+    out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = [0, 1, 77, 127]
+    deq = ofp8.dequantize(codes[rows].cpu().numpy(), scale[rows].cpu().numpy())
+    ref_out, ref_lse = oracle.decode_latent(w.q_prime[rows].cpu(), deq, w.seqlens[rows].cpu(), w.scale)
+    assert_out(to_np(out[rows]), ref_out, BF16_OUT_REL)
+    assert_lse(to_np(lse[rows]), ref_lse, BF16_LSE_ABS)
+
+
 # ---------------------------------------------------------------- absorbs, bf16
 
 @pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8)])

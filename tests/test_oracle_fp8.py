@@ -1,0 +1,67 @@
+"""Pins for the oracle's fp8 (OCP E4M3) codec and per-token quantiser.
+
+The pages define no quantised cache; these pin the oracle's fp8 helpers to
+the OCP E4M3 definition (closed forms, exhaustive round trips, the tie rule)
+and to the quantiser's stated properties, so that the GPU quantiser and the
+fp8 decode path are compared against something other than themselves.
+"""
+import numpy as np
+import pytest
+
+from oracle import fp8
+
+
+def test_e4m3_landmarks():
+    v = fp8.VALUES
+    assert v[0x00] == 0.0 and not np.signbit(v[0x00])
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])          # negative zero
+    assert v[0x01] == 2.0 ** -9                             # smallest subnormal
+    assert v[0x07] == 7 * 2.0 ** -9                         # largest subnormal
+    assert v[0x08] == 2.0 ** -6                             # smallest normal
+    assert v[0x38] == 1.0                                   # exponent field 7 = bias
+    assert v[0x39] == 1.125
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0           # largest finite
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])          # the only NaNs
+    assert np.isfinite(v).sum() == 254
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                         # codes 0..126 increase
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])     # sign bit
+
+
+def test_e4m3_round_trip_and_ties():
+    finite = np.array([c for c in range(256) if np.isfinite(fp8.VALUES[c])], np.uint8)
+    assert np.array_equal(fp8.encode(fp8.VALUES[finite].astype(np.float32)), finite)
+    # ties go to the even code
+    assert fp8.encode(np.float32([1.0625]))[0] == 0x38      # 1.0 | 1.125 -> 1.0
+    assert fp8.encode(np.float32([1.1875]))[0] == 0x3A      # 1.125 | 1.25 -> 1.25
+    assert fp8.encode(np.float32([1.5 * 2.0 ** -9]))[0] == 0x02  # subnormal tie
+    assert fp8.encode(np.float32([-1.0625]))[0] == 0xB8
+    # just off a tie goes to the nearer value
+    assert fp8.encode(np.nextafter(np.float32([1.0625]), np.float32(2)))[0] == 0x39
+    assert fp8.encode(np.float32([440.0]))[0] == 0x7E       # 432 | 448 -> 448
+    with pytest.raises(ValueError):
+        fp8.encode(np.float32([449.0]))
+
+
+def test_quantiser_properties():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 576)).astype(np.float32)
+    x[3] = 0.0                                               # all-zero row
+    x[7, 100] = 50.0                                         # one large entry
+    codes, scale = fp8.quantize_rows(x)
+    assert codes.shape == x.shape and codes.dtype == np.uint8 and scale.dtype == np.float32
+    amax = np.abs(x).max(axis=1)
+    np.testing.assert_array_equal(scale, (amax / np.float32(448)).astype(np.float32))
+    assert scale[3] == 0 and np.all(codes[3] == 0)
+    # each row's largest magnitude lands on +-448 (code 0x7E / 0xFE)
+    rows = [r for r in range(64) if r != 3]
+    arg = np.abs(x[rows]).argmax(axis=1)
+    assert np.all(codes[rows, arg] & 0x7F == 0x7E)
+    # dequantised error: at most half a step of the e4m3 grid
+    deq = fp8.dequantize(codes, scale)
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scale[:, None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+    # signs survive
+    nz = x != 0
+    assert np.all(np.sign(deq[nz]) == np.sign(x[nz]))
