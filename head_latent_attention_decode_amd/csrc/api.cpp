@@ -111,6 +111,9 @@ mla_status_t choose_fp8_schedule(int h, const mla_decode_config_t* cfg, Schedule
     const mla_status_t st = choose_schedule(MLA_DTYPE_BF16, h, &c, s);
     if (st != MLA_OK) return st;
     if (!bf16_variant_fp8(s->hpg, s->variant)) return MLA_ERR_UNSUPPORTED;
+    // the fp8 form needs 77 KB of LDS: two workgroups fit on a CU, so the
+    // automatic grid is twice as large
+    if (c.n_chunks == 0) s->n_chunks = round_down8(2 * kCUs / s->n_hg);
     return MLA_OK;
 }
 

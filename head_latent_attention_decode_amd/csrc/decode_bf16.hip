@@ -42,6 +42,25 @@ namespace mla355 {
 namespace {
 
 
+// fp8 staging layout: 16-byte chunk c of staged row r sits at chunk
+// f8chunk(c, f8sw(r)) (chunks 32..35, the rope key, stay inside their group of
+// four).  With the 592-byte row stride this keeps both fp8 operand reads free
+// of bank conflicts: the 8-byte score reads of rows 2i + sb (i = 0..15) and
+// the transposed 8-byte reads of 8 consecutive rows per 16 lanes.
+__device__ __forceinline__ int f8sw(int r) { return ((r >> 4) & 1) | ((r & 1) << 1); }
+__device__ __forceinline__ int f8chunk(int c, int sw) { return (c & ~3) | ((c & 3) ^ sw); }
+
+// Eight OCP e4m3 codes -> eight bf16 (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ bf16x8_t cvt8(unsigned long long codes)
+{
+    const unsigned lo = (unsigned)codes, hi = (unsigned)(codes >> 32);
+    const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
 template <int WH, int HS, int TS, int NT, int STAGES>
 struct Tiling {
     static constexpr int NW = HS * TS;
@@ -62,9 +81,11 @@ struct Tiling {
     static constexpr int MERGE_FLOATS = MBLK * Mfma<WH>::kAcc + 2;  // per lane
     // fp8 cache: a stage holds the tile's raw rows (576 B each) and per-token
     // scales; the conversion pass writes the bf16 tile above into one buffer
-    static constexpr int ROW8 = kDqk;                      // fp8 row bytes
-    static constexpr int STG8_BYTES = N * ROW8 + N * 4;
-    static constexpr int DMA8 = N * ROW8 / 1024 / NW;      // 1 KB DMA instructions per wave
+    static constexpr int ROW8 = kDqk;                      // fp8 row bytes in HBM
+    static constexpr int LROW8 = kDqk + 16;                // LDS stride of a staged fp8 row
+    static constexpr int STG8_BYTES = N * LROW8 + N * 4;   // rows + per-token scales
+    static constexpr int SCL8 = N * LROW8;                 // scales offset
+    static constexpr int DMA8 = N / NW;                    // one row per DMA instruction
     static_assert(N % NW == 0, "region A rows split evenly over waves");
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
     static_assert(STAGES == 2 || GROUPS_B % NW == 0, "exact vmcnt accounting needs even B split");
@@ -78,11 +99,12 @@ template <int WH, int HS, int TS, int NT, int STAGES, bool FP8>
 __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams p)
 {
     using T = Tiling<WH, HS, TS, NT, STAGES>;
-    static_assert(!FP8 || (STAGES == 2 && (T::N * T::ROW8) % (1024 * T::NW) == 0 && T::N <= 64 &&
-                           WH == 16 && NT % 16 == 0),
-                  "fp8 staging: two stages, whole DMA blocks per wave, one scale instruction, "
-                  "16-head waves over whole 16-row swizzle periods");
-    static_assert(!FP8 || STAGES * T::STG8_BYTES + T::TILE_BYTES <= 160 * 1024, "fp8 LDS budget");
+    static_assert(!FP8 || (STAGES == 2 && T::N % T::NW == 0 && T::N <= 64 && WH == 16 && NT == 32 &&
+                           HS == 1),
+                  "fp8 form: two stages, 16-head waves of 32 tokens, one scale per lane");
+    static_assert(!FP8 || 2 * STAGES * T::STG8_BYTES <= 160 * 1024, "fp8: two workgroups per CU");
+    static_assert(!FP8 || TS == 1 || (TS - 1) * HS * 64 * T::MERGE_FLOATS * 4 <= T::STG8_BYTES,
+                  "fp8 merge area");
     using M = Mfma<WH>;
     typedef typename M::acc_t acc_t;
 
@@ -154,6 +176,37 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
         }
     }
 
+    // fp8 operand reads (16-head waves, 32 tokens per wave and tile).
+    //  * scores: S block sb row i is token 2i + sb of the wave's 32 (so that the
+    //    weighted sum's k slots below are 8 consecutive tokens per 16 lanes).
+    //    Lane -> row 2 (lane & 15) + sb; at k step ks it reads logical chunk
+    //    2 ks + (g >> 1), byte 8 (g & 1), g = lane >> 4:
+    //    k8off[sb] + k8x[sb][ks & 1] + 64 (ks >> 1).
+    //  * weighted sum: ds_read_b64_tr_b8 hands output lane i (of 16) byte i % 8
+    //    of source lanes 2e + i / 8, e = 0..7.  Source lane (g, s) supplies
+    //    token 8g + perm(s >> 1) (perm = 0,2,4,6,1,3,5,7: the P^T slot order
+    //    the S layout above gives), bytes 16 mb + 8 (s & 1) .. +7, so output
+    //    lane i gets column 16 mb + i of the 8 tokens in slot order:
+    //    v8off + v8x[mb & 3] + 64 (mb >> 2).
+    int k8off[2] = {0, 0}, k8x[2][2] = {{0, 0}, {0, 0}}, v8off = 0, v8x[4] = {0, 0, 0, 0};
+    if (FP8) {
+        const int g = lane >> 4;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int row = tok0 + 2 * (lane & 15) + sb;
+            k8off[sb] = row * T::LROW8 + 8 * (g & 1);
+            const int sw = f8sw(row);
+#pragma unroll
+            for (int par = 0; par < 2; ++par) k8x[sb][par] = ((2 * par + (g >> 1)) ^ sw) << 4;
+        }
+        const int e = (lane & 15) >> 1;
+        const int row = tok0 + 8 * g + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+        v8off = row * T::LROW8 + 8 * (lane & 1);
+        const int sw = f8sw(row);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v8x[q] = (q ^ sw) << 4;
+    }
+
     while (true) {
         const int row_lo = pv.cu()[r];
         const int row_hi = pv.cu()[r + 1];
@@ -181,28 +234,32 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             }
         }
 
-        // fp8: the tile's rows are one contiguous run of N*576 bytes, copied
-        // as 1 KB blocks.  The buffer resource spans the valid rows only, and
-        // the whole offset is in the bounds-checked per-lane part, so a piece
-        // past the segment end reads as zero codes (finite; those tokens are
-        // masked).  Wave 0 also copies the N scales, 4 bytes per lane (past
-        // the valid rows they read as 0 the same way).
+        // fp8 staging: one DMA instruction per row (36 lanes x 16 bytes), row r
+        // at r * LROW8 with its 16-byte chunks XOR-swizzled by f8sw(r) (chunks
+        // 32..35, the rope key, inside their group of 4).  The buffer resource
+        // spans the valid rows only and the whole offset is in the
+        // bounds-checked per-lane part, so rows past the segment end read as
+        // zero codes (finite; those tokens are masked).  Wave 0 also copies
+        // the N scales, 4 bytes per lane (zero past the valid rows too).
         auto issue_tile8 = [&](auto SC, int tile) {
             const int t0 = tile * T::N;
             const int last = min(T::N, seg_len - t0) - 1;
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(seg_base + (size_t)t0 * T::ROW8), (short)0, (last + 1) * T::ROW8, kBufferFlags);
             lds_byte* st = stage_lds<T::STG8_BYTES, decltype(SC)::value>();
+            if (lane < kDqk / 16) {
 #pragma unroll
-            for (int j = 0; j < T::DMA8; ++j) {
-                const int blk = wave * T::DMA8 + j;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(st + blk * 1024), 16,
-                                                         (unsigned)(blk * 1024 + lane * 16), 0, 0, 0);
+                for (int j = 0; j < T::DMA8; ++j) {
+                    const int row = wave + j * T::NW;
+                    const int c = f8chunk(lane, f8sw(row));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(st + row * T::LROW8), 16,
+                                                             (unsigned)(row * T::ROW8 + c * 16), 0, 0, 0);
+                }
             }
             if (wave == 0 && lane < T::N) {  // one 4-byte scale per lane
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(seg_scale + t0), (short)0, (last + 1) * 4, kBufferFlags);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::N * T::ROW8), 4,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::SCL8), 4,
                                                          (unsigned)(lane * 4), 0, 0, 0);
             }
         };
@@ -268,41 +325,8 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             lds_exchange_barrier();
             if (it + STAGES - 1 < n_tiles) issue_tile(IC<(S + STAGES - 1) % STAGES>{}, it + STAGES - 1);
 
-            // fp8: each wave converts the staged codes of its own NT token rows
-            // (the only rows its score and weighted-sum reads touch) into the
-            // bf16 tile, in the layout and swizzles of a DMA'd bf16 tile (e4m3
-            // values are exact in bf16; each token's scale is applied to its
-            // score and probability below).  Region A: lane = 8-code chunk of
-            // row tok0 + k (the row swizzle depends on k only, since tok0 is a
-            // multiple of 16); region B: 8 chunks x 8 rows per step.
-            lds_byte* tb = FP8 ? stage_lds<T::TILE_BYTES, 8>() : stage_lds<T::TILE_BYTES, S>();
+            lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
             const lds_byte* sg = stage_lds<T::STG8_BYTES, S>();
-            if (FP8) {
-                auto cvt8 = [](unsigned long long codes) -> bf16x8_t {
-                    const unsigned lo = (unsigned)codes, hi = (unsigned)(codes >> 32);
-                    const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-                    const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-                    const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-                    const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-                    return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-                };
-                const lds_byte* srcA = sg + tok0 * T::ROW8 + lane * 8;
-                lds_byte* dstA = tb + tok0 * 1024;
-#pragma unroll
-                for (int k = 0; k < NT; ++k) {
-                    const unsigned long long codes = *(const LDS_AS unsigned long long*)(srcA + k * T::ROW8);
-                    *(LDS_AS bf16x8_t*)(dstA + k * 1024 + ((lane ^ M::xa(k & 15)) << 4)) = cvt8(codes);
-                }
-                const int cb = lane & 7;
-#pragma unroll
-                for (int j = 0; j < NT / 8; ++j) {
-                    const int k = (lane >> 3) + 8 * j;
-                    const unsigned long long codes =
-                        *(const LDS_AS unsigned long long*)(sg + (tok0 + k) * T::ROW8 + kDc + cb * 8);
-                    *(LDS_AS bf16x8_t*)(tb + T::A_BYTES + (tok0 + k) * 128 + ((cb ^ xb(k & 15)) << 4)) = cvt8(codes);
-                }
-                lds_wave_sync();  // this wave's converted rows written before it reads them
-            }
             const int tvalid = seg_len - it * T::N - tok0;  // valid tokens for this wave (may be <= 0)
 
             // ---- S^T = K . Q^T -------------------------------------------------
@@ -318,17 +342,22 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
                 if (ks < T::KSTEPS_A) return tb + koffA[ks % NQA] + (ks / NQA) * 256 + sb * WH * 1024;
                 return tb + koffB[ks - T::KSTEPS_A] + sb * WH * 128;
             };
+            auto k_frag = [&](int idx) -> bf16x8_t {
+                if (!FP8) return *(const LDS_AS bf16x8_t*)k_addr(idx);
+                const int ks = idx / T::SBLK, sb = idx % T::SBLK;
+                return cvt8(*(const LDS_AS unsigned long long*)(sg + k8off[sb] + k8x[sb][ks & 1] + 64 * (ks >> 1)));
+            };
             acc_t sacc[T::SBLK][2];
 #pragma unroll
             for (int sb = 0; sb < T::SBLK; ++sb) sacc[sb][0] = sacc[sb][1] = (acc_t){};
             bf16x8_t kring[PF];
 #pragma unroll
-            for (int i = 0; i < PF; ++i) kring[i] = *(const LDS_AS bf16x8_t*)k_addr(i);
+            for (int i = 0; i < PF; ++i) kring[i] = k_frag(i);
 #pragma unroll
             for (int idx = 0; idx < NSTEP; ++idx) {
                 const int ks = idx / T::SBLK, sb = idx % T::SBLK;
                 const bf16x8_t kf = kring[idx % PF];
-                if (idx + PF < NSTEP) kring[idx % PF] = *(const LDS_AS bf16x8_t*)k_addr(idx + PF);
+                if (idx + PF < NSTEP) kring[idx % PF] = k_frag(idx + PF);
                 sacc[sb][ks & 1] = M::mma(kf, qf[ks], sacc[sb][ks & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -346,8 +375,8 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             for (int sb = 0; sb < T::SBLK; ++sb)
 #pragma unroll
                 for (int i = 0; i < M::kAcc; ++i) {
-                    const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
-                    tsc[sb][i] = FP8 ? *(const LDS_AS float*)(sg + T::N * T::ROW8 + (tok0 + sb * WH + toff) * 4)
+                    // fp8: entry (sb, i) is token 2 (4 grp + i) + sb of the wave's 32
+                    tsc[sb][i] = FP8 ? *(const LDS_AS float*)(sg + T::SCL8 + (tok0 + 2 * (grp * 4 + i) + sb) * 4)
                                      : 1.0f;
                 }
 #pragma unroll
@@ -355,8 +384,9 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
 #pragma unroll
                 for (int i = 0; i < M::kAcc; ++i) {
                     const int toff = (WH == 16) ? (grp * 4 + i) : ((i >> 2) * 8 + grp * 4 + (i & 3));
+                    const int tok = FP8 ? 2 * (grp * 4 + i) + sb : sb * WH + toff;
                     float v = sfin[sb][i] * (FP8 ? p.scale_log2 * tsc[sb][i] : p.scale_log2);
-                    if (!full && sb * WH + toff >= tvalid) v = -INFINITY;
+                    if (!full && tok >= tvalid) v = -INFINITY;
                     sfin[sb][i] = v;
                     tmax = fmaxf(tmax, v);
                 }
@@ -398,6 +428,12 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             constexpr int PFV = 4;
             auto v_frag = [&](int idx) -> bf16x8_t {
                 const int u = idx / T::MBLK, mb = idx % T::MBLK;
+                if (FP8) {
+                    typedef int v2i_t __attribute__((ext_vector_type(2)));
+                    const v2i_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (LDS_AS v2i_t*)(sg + v8off + v8x[mb & 3] + 64 * (mb >> 2)));
+                    return cvt8(__builtin_bit_cast(unsigned long long, c));
+                }
                 const int q = mb % NQV;
                 const int blk = (mb / NQV) * 256 + u * TPU * 1024;
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -437,7 +473,7 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             // subgroup merges them.  The merge area overlays the tile stages,
             // so first every wave must have finished reading the last tile.
             wg_barrier();
-            float* area = (float*)(FP8 ? stage_lds<T::TILE_BYTES, 8>() : stage_lds<T::TILE_BYTES, 0>());
+            float* area = (float*)(FP8 ? stage_lds<T::STG8_BYTES, 0>() : stage_lds<T::TILE_BYTES, 0>());
             if (ts > 0) {
                 float* dst = area + ((size_t)((ts - 1) * HS + hs) * T::MERGE_FLOATS) * 64;
                 dst[lane] = m_run;

@@ -196,5 +196,6 @@ def test_fp8_validation_and_queries(mla):
     assert mla.mla_decode_fp8_kernel_name(128) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
     assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 128}) is None
     assert mla.mla_decode_fp8_kernel_name(16, {"heads_per_group": 16, "variant": 2}) is None
+    # two resident workgroups per CU: twice the chunks of the bf16 schedule
     assert mla.mla_decode_fp8_workspace_bytes(128, 16, 8192) == \
-        mla.mla_decode_workspace_bytes(torch.bfloat16, 128, 16, 8192)
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 128, 16, 8192, {"n_chunks": 512})
