@@ -60,6 +60,11 @@ struct WideTiling {
     static constexpr int KS = kDqk / 16;               // 36 score k-steps
     static constexpr int KSA = kDc / 16;               // 32 of them in region A
     static constexpr int MBLK = kDc / 32;              // 16 output blocks of 32 columns
+    // Epilogue staging: 32 rows of 256 outputs (bf16) per wave, rows padded
+    // by 16 B so that the rows of one accumulator write start in distinct
+    // bank groups; two waves per ring stage.
+    static constexpr int STG_ROW = 512 + 16;
+    static_assert(2 * 32 * STG_ROW <= TILE_BYTES && NW <= 2 * STAGES, "epilogue staging fits the ring");
     static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
     static_assert(GROUPS_B % NW == 0, "region-B groups split evenly over waves");
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
@@ -367,33 +372,54 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
 
         // ---- segment epilogue ----------------------------------------------
         // A row finished here writes out/lse; otherwise its slot's partial
-        // (normalised, bf16) and partial lse.
+        // (normalised, bf16) and partial lse.  A store straight from the
+        // accumulator layout would write 16 bytes into each of 32 head rows;
+        // instead each wave stages half of its 32 x 512 outputs at a time in
+        // LDS (the tile ring is free once every wave is past the last tile)
+        // and stores whole 512-byte half rows.
         l_run += __shfl_xor(l_run, 32, 64);
+        lds_exchange_barrier();  // no DMA is in flight after the last tile
         {
             // The lane's head and column group are derived again here from the
             // thread index (opaque to the compiler) instead of being kept live
             // across the tile loop, where every register is taken.
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
+            const int e_lane = tid & 63;
             const int e_grp = (tid >> 5) & 1;
-            const int e_head = hg * T::HG + wave * 32 + (tid & 31);
-            if (e_head < p.h) {
-                const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-                const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-                __bf16* orow = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
-                                          : (__bf16*)p.po + (size_t)slot * p.h * kDc) + e_head * kDc + e_grp * 4;
+            const int e_hl = tid & 31;
+            const int head0 = hg * T::HG + wave * 32;
+            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+            const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+            __bf16* obase = (final_out ? (__bf16*)p.out + (size_t)r * p.h * kDc
+                                       : (__bf16*)p.po + (size_t)slot * p.h * kDc) + (size_t)head0 * kDc;
+            lds_byte* stg = ((wave >> 1) == 0 ? stage_lds<T::TILE_BYTES, 0>() : stage_lds<T::TILE_BYTES, 1>()) +
+                            (wave & 1) * 32 * T::STG_ROW;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
                 // accumulator entry e of block mb: column 32mb + (e/4)*8 + 4grp + e%4
 #pragma unroll
-                for (int mb = 0; mb < T::MBLK; ++mb)
+                for (int mb = half * T::MBLK / 2; mb < (half + 1) * T::MBLK / 2; ++mb)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         bf16x4_t v;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[mb][q4 * 4 + e] * inv);
-                        *(bf16x4_t*)(orow + mb * 32 + q4 * 8) = v;
+                        const int col = (mb - half * T::MBLK / 2) * 32 + q4 * 8 + e_grp * 4;
+                        *(LDS_AS bf16x4_t*)(stg + e_hl * T::STG_ROW + 2 * col) = v;
                     }
-                if (e_grp == 0) (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[e_head] = lse_v;
+                // a wave's LDS accesses complete in order: the reads below see
+                // the writes above, and the next half's writes follow these reads
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 2 * i + (e_lane >> 5);
+                    const bf16x8_t v = *(const LDS_AS bf16x8_t*)(stg + row * T::STG_ROW + 16 * e_hl);
+                    if (head0 + row < p.h)
+                        *(bf16x8_t*)(obase + (size_t)row * kDc + half * (kDc / 2) + 8 * e_hl) = v;
+                }
             }
+            if (e_grp == 0 && head0 + e_hl < p.h)
+                (final_out ? p.lse + (size_t)r * p.h : p.plse + (size_t)slot * p.h)[head0 + e_hl] = lse_v;
         }
 
         pos = seg_end;
