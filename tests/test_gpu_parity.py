@@ -106,6 +106,34 @@ def test_bf16_edges_every_output(mla, h, cfg):
         assert torch.all(torch.isneginf(lse[EDGE_LENS.index(0)]))
 
 
+RESCALE_CASES = [
+    (128, None), (128, {"heads_per_group": 128, "variant": 3}), (128, {"heads_per_group": 128, "variant": 5}),
+    (64, {"heads_per_group": 64, "variant": 6}), (64, {"heads_per_group": 64, "variant": 2}),
+    (32, {"heads_per_group": 32, "variant": 4}), (128, {"heads_per_group": 16}),
+]
+
+
+@pytest.mark.parametrize("h,cfg", RESCALE_CASES, ids=[_case_id(c) for c in RESCALE_CASES])
+def test_bf16_running_max_growth(mla, h, cfg):
+    # Scores that grow along the tokens for some heads only: the running max
+    # of those heads jumps by more than the lazy-rescale threshold tile after
+    # tile, while the other heads never rescale.
+    w = workloads.make_custom(4, h, [700, 257, 1000, 33], seed=61 + h, device="cuda")
+    t = torch.arange(w.t_max, device="cuda", dtype=torch.float32)
+    w.cache[:, :, 575] = (0.25 * t).to(torch.bfloat16)[None, :]
+    slope = torch.tensor([16.0, 4.0, 1.0, 0.0, -4.0, 0.5, 8.0, -1.0], device="cuda")
+    per_head = slope[torch.arange(h, device="cuda") % 8]
+    # heads 32..63 and 96..127 (second and fourth group of 32) never grow
+    per_head = torch.where((torch.arange(h, device="cuda") // 32) % 2 == 1, -per_head.abs(), per_head)
+    w.q_prime[:, :, 575] = per_head.to(torch.bfloat16)[None, :]
+    workloads.poison_tail(w.cache, w.seqlens)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}):
+        c = dict(cfg or {})
+        c.update(extra)
+        out, lse = _run(mla, w, c or None)
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
+
+
 def test_bf16_split_invariance_and_determinism(mla):
     w = workloads.make_custom(5, 128, [3000, 17, 4096, 1, 2500], seed=7, device="cuda")
     outs = []
