@@ -86,6 +86,8 @@ class Oracle:
         ci, cd = ctypes.c_int, ctypes.c_double
         lib.oracle_decode_latent.argtypes = [ci, ci, ci, ci, ci, dp, dp, ip, cd, dp, dp, dp]
         lib.oracle_decode_latent.restype = None
+        lib.oracle_decode_latent_causal.argtypes = [ci, ci, ci, ci, ci, ci, dp, dp, ip, cd, dp, dp]
+        lib.oracle_decode_latent_causal.restype = None
         lib.oracle_decode_unabsorbed.argtypes = [ci, ci, ci, ci, ci, ci, ci, dp, dp, dp, dp,
                                                  dp, ip, cd, ip, ci, dp, dp, dp, dp]
         lib.oracle_decode_unabsorbed.restype = None
@@ -121,6 +123,26 @@ class Oracle:
         self.lib.oracle_decode_latent(b, h, t_max, d_c, d_r, _dp(q), _dp(c), _ip(sl),
                                       float(scale), _dp(out), _dp(lse), _dp(sc))
         return (out, lse, sc) if want_scores else (out, lse)
+
+    def decode_latent_causal(self, q_prime, cache, seqlens, scale, d_c=D_C):
+        """Latent form with several query tokens per row (causal reading).
+
+        q_prime [b,q_len,h,d_c+d_r], cache [b,t_max,d_c+d_r], seqlens [b]: new
+        token i attends to the first seqlens[b] - q_len + 1 + i rows.  Returns
+        (out [b,q_len,h,d_c], lse [b,q_len,h]).
+        """
+        q = _f64(q_prime)
+        c = _f64(cache)
+        sl = _i32(seqlens)
+        b, q_len, h, d = q.shape
+        assert c.ndim == 3 and c.shape[0] == b and c.shape[2] == d, (q.shape, c.shape)
+        assert sl.shape == (b,)
+        t_max = c.shape[1]
+        out = np.empty((b, q_len, h, d_c), np.float64)
+        lse = np.empty((b, q_len, h), np.float64)
+        self.lib.oracle_decode_latent_causal(b, q_len, h, t_max, d_c, d - d_c, _dp(q), _dp(c),
+                                             _ip(sl), float(scale), _dp(out), _dp(lse))
+        return out, lse
 
     def decode_unabsorbed(self, q_nope, q_rope, w_uk, w_uv, cache, seqlens, scale, heads=None,
                           want_scores=False):
@@ -188,6 +210,10 @@ def decode_latent(*a, **k):
 
 def decode_unabsorbed(*a, **k):
     return default().decode_unabsorbed(*a, **k)
+
+
+def decode_latent_causal(*a, **k):
+    return default().decode_latent_causal(*a, **k)
 
 
 def absorb_q(*a, **k):

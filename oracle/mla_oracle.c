@@ -34,6 +34,14 @@
  * Which tokens are attended: exactly the first seqlens[b] cached rows, no
  * causal mask (the glossary's check attends only to the earlier tokens).
  * seqlens[b] == 0 yields out = 0, lse = -inf.
+ *
+ * Several query tokens per row (oracle_decode_latent_causal): the glossary's
+ * production notes say prefill and decode take different paths, and the
+ * Polish overview gives attention's O(n^2 d) cost (every token against every
+ * earlier one) without spelling out a mask.  Reading: the q_len new tokens
+ * are the last q_len of the seqlens[b] cached rows, and new token i (0-based)
+ * attends to the rows up to and including its own, i.e. the first
+ * seqlens[b] - q_len + 1 + i rows (none if that is not positive).
  */
 #include <math.h>
 #include <omp.h>
@@ -190,6 +198,49 @@ void oracle_decode_unabsorbed(int b, int h, int t_max, int d_c, int d_r, int d_k
         free(s);
         free(p);
         free(kv);
+    }
+}
+
+/*
+ * Latent form with q_len query tokens per row and the causal reading above.
+ * q_prime [b, q_len, h, d_c + d_r], out [b, q_len, h, d_c], lse [b, q_len, h]:
+ *   n_i = seqlens[b] - q_len + 1 + i   (clamped to [0, seqlens[b]])
+ *   s_t = scale * sum_i q'[b,i,h,:] . row_t,  t < n_i
+ *   p   = softmax(s),  out = sum_t p_t row_t[0:d_c],  lse = log sum_t exp(s_t)
+ */
+void oracle_decode_latent_causal(int b, int q_len, int h, int t_max, int d_c, int d_r,
+                                 const double* q_prime, const double* cache,
+                                 const int32_t* seqlens, double scale,
+                                 double* out, double* lse)
+{
+    const int d = d_c + d_r;
+    const long rows = (long)b * q_len * h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long r = 0; r < rows; ++r) {
+        const int bi = (int)(r / ((long)q_len * h));
+        const int qi = (int)((r / h) % q_len);
+        const int L = clamp_len(seqlens[bi], t_max);
+        int n = L - q_len + 1 + qi;
+        if (n < 0) n = 0;
+        if (n > L) n = L;
+        const double* q = q_prime + IDX2(r, 0, d);
+        double* o = out + IDX2(r, 0, d_c);
+        double* s = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+        double* p = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+        for (int t = 0; t < n; ++t) {
+            const double* row = cache + IDX3(bi, t, 0, t_max, d);
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += q[i] * row[i];
+            s[t] = scale * acc;
+        }
+        lse[r] = softmax_f64(s, n, p);
+        for (int c = 0; c < d_c; ++c) o[c] = 0.0;
+        for (int t = 0; t < n; ++t) {
+            const double* row = cache + IDX3(bi, t, 0, t_max, d);
+            for (int c = 0; c < d_c; ++c) o[c] += p[t] * row[c];
+        }
+        free(s);
+        free(p);
     }
 }
 

@@ -328,6 +328,76 @@ def pin_empty_sequence(orc, seed=23):
     assert np.all(np.isfinite(lse[1]))
 
 
+def _causal_counts(lens, q_len):
+    """Rows new token i of each batch row may see: L - q_len + 1 + i, clamped to [0, L]."""
+    return np.clip(np.asarray(lens)[:, None] - q_len + 1 + np.arange(q_len)[None, :], 0,
+                   np.asarray(lens)[:, None])
+
+
+def pin_causal_vs_sdpa(orc, seed=24):
+    """Several query tokens per row == torch SDPA (fp64) with an explicit
+    boolean mask that lets new token i see rows t <= L - q_len + i."""
+    g = _rng(seed)
+    b, q_len, h, t_max = 3, 4, 3, 40
+    lens = np.array([40, 9, 2], np.int32)  # the last row has fewer rows than new tokens
+    cache = g.standard_normal((b, t_max, 576))
+    qp = g.standard_normal((b, q_len, h, 576))
+    out, lse = orc.decode_latent_causal(qp, cache, lens, SCALE)
+    n = _causal_counts(lens, q_len)
+    for i in range(b):
+        L = int(lens[i])
+        q = torch.from_numpy(qp[i].transpose(1, 0, 2).copy())[None]  # [1, h, q_len, d]
+        k = torch.from_numpy(cache[i, :L])[None, None].expand(1, h, L, 576).contiguous()
+        v = torch.from_numpy(cache[i, :L, :512])[None, None].expand(1, h, L, 512).contiguous()
+        mask = torch.from_numpy(np.arange(L)[None, :] < n[i][:, None])  # [q_len, L]
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=SCALE)
+        o = o[0].numpy().transpose(1, 0, 2)  # [q_len, h, 512]
+        for qi in range(q_len):
+            if n[i, qi] > 0:
+                _close(out[i, qi], o[qi], 1e-12, "causal out vs masked SDPA")
+                s = SCALE * (qp[i, qi] @ cache[i, :n[i, qi]].T)  # [h, n]
+                m = s.max(1)
+                _close(lse[i, qi], m + np.log(np.exp(s - m[:, None]).sum(1)), 1e-12, "causal lse")
+            else:
+                assert np.all(out[i, qi] == 0.0) and np.all(np.isneginf(lse[i, qi])), "empty prefix"
+
+
+def pin_causal_zero_query(orc, seed=25):
+    """q' = 0 with several new tokens: token i averages exactly its visible
+    prefix of n_i rows and lse = ln n_i."""
+    g = _rng(seed)
+    lens = np.array([10, 3], np.int32)
+    q_len = 3
+    cache = g.standard_normal((2, 10, 576))
+    out, lse = orc.decode_latent_causal(np.zeros((2, q_len, 2, 576)), cache, lens, SCALE)
+    n = _causal_counts(lens, q_len)
+    for i in range(2):
+        for qi in range(q_len):
+            _close(lse[i, qi], np.full(2, math.log(n[i, qi])), 1e-12, "lse = ln n_i")
+            _close(out[i, qi], np.broadcast_to(cache[i, :n[i, qi], :512].mean(0), (2, 512)), 1e-12,
+                   "out = mean of the visible prefix")
+
+
+def pin_causal_future_rows_unseen(orc, seed=26):
+    """A NaN written into the row of new token j reaches exactly the new tokens
+    j, j+1, ... and leaves every earlier one unchanged."""
+    g = _rng(seed)
+    L, q_len, h = 12, 4, 2
+    cache = g.standard_normal((1, L, 576))
+    qp = g.standard_normal((1, q_len, h, 576))
+    lens = np.array([L], np.int32)
+    ref, _ = orc.decode_latent_causal(qp, cache, lens, SCALE)
+    for j in range(q_len):
+        bad = cache.copy()
+        bad[0, L - q_len + j] = np.nan
+        out, _ = orc.decode_latent_causal(qp, bad, lens, SCALE)
+        for qi in range(q_len):
+            if qi < j:
+                _close(out[0, qi], ref[0, qi], 0.0, "earlier token unaffected")
+            else:
+                assert np.all(np.isnan(out[0, qi])), "token %d must see row of token %d" % (qi, j)
+
+
 ALL_PINS = [
     pin_glossary_toy_identities,
     pin_identities_c1_dims,
@@ -343,4 +413,7 @@ ALL_PINS = [
     pin_absorbs_vs_numpy,
     pin_unabsorbed_identity_weights_vs_sdpa,
     pin_empty_sequence,
+    pin_causal_vs_sdpa,
+    pin_causal_zero_query,
+    pin_causal_future_rows_unseen,
 ]

@@ -29,6 +29,9 @@ MUTANTS = [
      "qp[d_c + r] = q_rope[IDX2(bh, 0, d_r)];", 0),
     ("wrong_head_in_expanded_query", "const double* qn = q_nope + IDX3(bi, hi, 0, h, d_k);",
      "const double* qn = q_nope + IDX3(bi, 0, 0, h, d_k);", 0),
+    ("causal_limit_off_by_one", "int n = L - q_len + 1 + qi;", "int n = L - q_len + qi;", 0),
+    ("causal_no_mask", "int n = L - q_len + 1 + qi;", "int n = L;", 0),
+    ("causal_reversed_tokens", "int n = L - q_len + 1 + qi;", "int n = L - qi;", 0),
 ]
 
 
