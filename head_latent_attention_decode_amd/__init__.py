@@ -86,13 +86,20 @@ _lib.mla_decode_fp8_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp, _cf, _vp, 
 _lib.mla_decode_paged_ex.restype = _ci
 _lib.mla_decode_paged_ex.argtypes = [_ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp,
                                      _vp, _vp, _sz, ctypes.POINTER(MLAConfig), _vp]
+_lib.mla_decode_mtp_workspace_bytes.restype = _sz
+_lib.mla_decode_mtp_workspace_bytes.argtypes = [_ci, _ci, _ci, _ci, _ci]
+_lib.mla_decode_mtp_kernel_name.restype = ctypes.c_char_p
+_lib.mla_decode_mtp_kernel_name.argtypes = [_ci, _ci, _ci]
+_lib.mla_decode_mtp.restype = _ci
+_lib.mla_decode_mtp.argtypes = [_ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
                     "mla_decode_ex", "mla_decode_kernel_name", "mla_decode_paged_workspace_bytes",
                     "mla_decode_paged", "mla_decode_paged_ex", "mla_decode_paged_kernel_name",
                     "mla_quantize_cache_fp8", "mla_decode_fp8_workspace_bytes", "mla_decode_fp8",
-                    "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name")
+                    "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name",
+                    "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name")
 
 
 class MLAError(RuntimeError):
@@ -229,6 +236,55 @@ def mla_decode(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, works
     else:
         st = _lib.mla_decode_ex(_dtype_code(dt), b, h, t_max, *args, _cfg(config), _stream(stream))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_mtp_kernel_name(q_len: int, h: int):
+    """Name of the attention kernel mla_decode_mtp would launch (pure host); None if rejected."""
+    name = _lib.mla_decode_mtp_kernel_name(MLA_DTYPE_BF16, q_len, h)
+    return None if name is None else name.decode()
+
+
+def mla_decode_mtp_workspace_bytes(b: int, q_len: int, h: int, t_max: int) -> int:
+    """Bytes of workspace mla_decode_mtp needs (pure host computation, no GPU)."""
+    return int(_lib.mla_decode_mtp_workspace_bytes(MLA_DTYPE_BF16, b, q_len, h, t_max))
+
+
+def mla_decode_mtp(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, workspace=None,
+                   stream=None):
+    """Latent-form decode of q_len causal query tokens per row (bf16).
+
+    q_prime [b,q_len,h,576], cache [b,t_max,576], seqlens [b] int32 on the GPU
+    (cached rows, the q_len new ones included).  Returns (out [b,q_len,h,512],
+    lse [b,q_len,h] fp32).
+    """
+    b, q_len, h, _ = q_prime.shape
+    t_max = cache.shape[1]
+    dt = q_prime.dtype
+    dev = q_prime.device
+    if dt != torch.bfloat16:
+        raise TypeError("mla_decode_mtp takes bf16 tensors")
+    if out is None:
+        out = torch.empty((b, q_len, h, D_C), dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((b, q_len, h), dtype=torch.float32, device=dev)
+    need = mla_decode_mtp_workspace_bytes(b, q_len, h, t_max)
+    if need == 0:
+        raise ValueError("invalid problem: b=%d q_len=%d h=%d t_max=%d" % (b, q_len, h, t_max))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    st = _lib.mla_decode_mtp(MLA_DTYPE_BF16, b, q_len, h, t_max,
+                             _dev(q_prime, "q_prime", (b, q_len, h, D_QK), dt),
+                             _dev(cache, "cache", (b, t_max, D_QK), dt),
+                             _dev(seqlens, "seqlens", (b,), torch.int32),
+                             ctypes.c_float(float(softmax_scale)),
+                             _dev(out, "out", (b, q_len, h, D_C), dt),
+                             _dev(lse, "lse", (b, q_len, h), torch.float32),
+                             ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                             _stream(stream))
+    _check(st, "mla_decode_mtp")
     return out, lse
 
 

@@ -117,6 +117,24 @@ mla_status_t choose_fp8_schedule(int h, const mla_decode_config_t* cfg, Schedule
     return MLA_OK;
 }
 
+// Schedule for q_len causal query tokens per row (q_len > 1): the wide-wave
+// kernels, whose query rows are the q_len * h (token, head) pairs of a batch
+// row, 32 per wave.
+struct MtpSchedule {
+    int nw;         // waves per workgroup (32 query rows each)
+    int n_hg;       // groups of 32 * nw query rows
+    int n_chunks;
+};
+
+MtpSchedule choose_mtp_schedule(int rows)
+{
+    MtpSchedule s;
+    s.nw = rows > 64 ? 4 : rows > 32 ? 2 : 1;
+    s.n_hg = (rows + 32 * s.nw - 1) / (32 * s.nw);
+    s.n_chunks = round_down8(kCUs / s.n_hg);
+    return s;
+}
+
 bool dims_ok(int b, int h, int t_max)
 {
     if (b <= 0 || h <= 0 || t_max < 0) return false;
@@ -202,6 +220,8 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     p.cache_scale = nullptr;
     p.seqlens = seqlens;
     p.num_blocks = p.block_size = p.max_blocks = 0;
+    p.q_len = 1;
+    p.heads_per_token = h;
     p.b = b;
     p.h = h;
     p.t_max = t_max;
@@ -231,6 +251,87 @@ mla_status_t mla_decode(mla_dtype_t dt, int b, int h, int t_max, const void* q_p
 {
     return mla_decode_ex(dt, b, h, t_max, q_prime, cache, seqlens, softmax_scale, out, lse,
                          workspace, workspace_bytes, nullptr, stream);
+}
+
+bool mtp_dims_ok(int b, int q_len, int h, int t_max)
+{
+    if (q_len <= 0 || h <= 0 || (int64_t)q_len * h > ((int64_t)1 << 20)) return false;
+    return dims_ok(b, q_len * h, t_max);
+}
+
+size_t mla_decode_mtp_workspace_bytes(mla_dtype_t dt, int b, int q_len, int h, int t_max)
+{
+    if (dt != MLA_DTYPE_BF16 || !mtp_dims_ok(b, q_len, h, t_max)) return 0;
+    if (q_len == 1) return mla_decode_workspace_bytes(dt, b, h, t_max);
+    const MtpSchedule s = choose_mtp_schedule(q_len * h);
+    return workspace_layout(b, q_len * h, s.n_chunks, 2).total;
+}
+
+const char* mla_decode_mtp_kernel_name(mla_dtype_t dt, int q_len, int h)
+{
+    if (dt != MLA_DTYPE_BF16 || q_len <= 0 || h <= 0 || (int64_t)q_len * h > ((int64_t)1 << 20))
+        return nullptr;
+    if (q_len == 1) return mla_decode_kernel_name(dt, h, nullptr);
+    switch (choose_mtp_schedule(q_len * h).nw) {
+    case 4: return "decode_wide_causal_kernel<4, 2, false>";
+    case 2: return "decode_wide_causal_kernel<2, 2, false>";
+    default: return "decode_wide_causal_kernel<1, 3, false>";
+    }
+}
+
+mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, const void* q_prime,
+                            const void* cache, const int32_t* seqlens, float softmax_scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream)
+{
+    if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
+    if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+    if (!mtp_dims_ok(b, q_len, h, t_max)) return MLA_ERR_INVALID_ARGUMENT;
+    if (q_len == 1)
+        return mla_decode_ex(dt, b, h, t_max, q_prime, cache, seqlens, softmax_scale, out, lse,
+                             workspace, workspace_bytes, nullptr, stream);
+    if (!q_prime || !cache || !seqlens || !out || !lse || !workspace) return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_prime) || !aligned16(cache) || !aligned16(seqlens) || !aligned16(out) ||
+        !aligned16(lse) || ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    const int rows = q_len * h;
+    const MtpSchedule s = choose_mtp_schedule(rows);
+    const WorkspaceLayout w = workspace_layout(b, rows, s.n_chunks, 2);
+    if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    int32_t* plan = (int32_t*)ws;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = cache;
+    p.plan = plan;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (void*)(ws + w.po_off);
+    p.block_table = nullptr;
+    p.cache_scale = nullptr;
+    p.seqlens = seqlens;
+    p.num_blocks = p.block_size = p.max_blocks = 0;
+    p.q_len = q_len;
+    p.heads_per_token = h;
+    p.b = b;
+    p.h = rows;
+    p.t_max = t_max;
+    p.n_chunks = s.n_chunks;
+    p.n_hg = s.n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    hipError_t e = launch_plan(seqlens, b, rows, t_max, s.n_chunks, 32, 1, plan, true, out, lse, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    e = s.nw == 4   ? launch_decode_wide_causal<4, 2>(p, hs)
+        : s.nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
+                    : launch_decode_wide_causal<1, 3>(p, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    e = launch_combine(true, plan, b, rows, p.plse, p.po, out, lse, hs);
+    return hip_status(e);
 }
 
 size_t mla_decode_paged_workspace_bytes(mla_dtype_t dt, int b, int h, int num_blocks,
@@ -292,6 +393,8 @@ mla_status_t mla_decode_paged_ex(mla_dtype_t dt, int b, int h, const void* q_pri
     p.num_blocks = num_blocks;
     p.block_size = block_size;
     p.max_blocks = max_blocks;
+    p.q_len = 1;
+    p.heads_per_token = h;
     p.b = b;
     p.h = h;
     p.t_max = t_max;
@@ -382,6 +485,8 @@ mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, con
     p.cache_scale = cache_scale;
     p.seqlens = seqlens;
     p.num_blocks = p.block_size = p.max_blocks = 0;
+    p.q_len = 1;
+    p.heads_per_token = h;
     p.b = b;
     p.h = h;
     p.t_max = t_max;

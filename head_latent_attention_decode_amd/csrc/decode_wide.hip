@@ -77,8 +77,12 @@ struct WideTiling {
 // while this one runs: a uniform index loads through the scalar cache.
 typedef const __attribute__((address_space(4))) int32_t cint32_t;
 
-template <int NW, int STAGES, bool PAGED>
-__global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
+// Kernel body.  CAUSAL: the "heads" are q_len new tokens x heads_per_token
+// heads (q' [b, q_len, h, 576] read as [b, q_len*h, 576]), and new token i of
+// a row of L cached rows (the new ones last) attends to its first
+// L - q_len + 1 + i rows only.
+template <int NW, int STAGES, bool PAGED, bool CAUSAL>
+__device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
 {
     using T = WideTiling<NW, STAGES>;
     using M = Mfma<32>;
@@ -152,6 +156,13 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
             // the plan covers lengths rounded up to whole tiles: mask the rest
             const int L = min(max(plan_at(p.seqlens + r), 0), p.t_max);
             seg_len = max(0, min(seg_len, L - seg_a));
+        }
+        // CAUSAL: tokens of this segment the lane's query row may see (any
+        // value: <= 0 none, >= seg_len all)
+        int c_lim = 0;
+        if constexpr (CAUSAL) {
+            const int L = PAGED ? min(max(plan_at(p.seqlens + r), 0), p.t_max) : row_hi - row_lo;
+            c_lim = L - p.q_len + 1 + head / p.heads_per_token - seg_a;
         }
         const int split_j = k - row_lo / chunk;
         const bool final_out = plan_at(pv.nsplit() + r) == 1;
@@ -303,7 +314,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
 
             // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
             const int tvalid = __builtin_amdgcn_readfirstlane(seg_len - i * T::N);
-            if (tvalid < T::N) {
+            if constexpr (CAUSAL) {
+                const int lim_l = min(tvalid, c_lim - i * T::N);
+                if (__any(lim_l < T::N)) {
+                    const int lim = lim_l - 4 * grp;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if ((e >> 2) * 8 + (e & 3) >= lim) sacc[e] = -INFINITY;
+                }
+            } else if (tvalid < T::N) {
                 const int lim = tvalid - 4 * grp;
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
@@ -430,6 +449,18 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
     }
 }
 
+template <int NW, int STAGES, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
+{
+    decode_wide_body<NW, STAGES, PAGED, false>(p);
+}
+
+template <int NW, int STAGES, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void decode_wide_causal_kernel(DecodeParams p)
+{
+    decode_wide_body<NW, STAGES, PAGED, true>(p);
+}
+
 }  // namespace
 
 template <int NW, int STAGES>
@@ -450,5 +481,21 @@ template hipError_t launch_decode_wide<4, 2>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<2, 3>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<2, 2>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_wide<1, 3>(const DecodeParams&, hipStream_t);
+
+template <int NW, int STAGES>
+hipError_t launch_decode_wide_causal(const DecodeParams& p, hipStream_t stream)
+{
+    using T = WideTiling<NW, STAGES>;
+    const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
+    if (p.block_table != nullptr)
+        decode_wide_causal_kernel<NW, STAGES, true><<<grid, T::THREADS, 0, stream>>>(p);
+    else
+        decode_wide_causal_kernel<NW, STAGES, false><<<grid, T::THREADS, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template hipError_t launch_decode_wide_causal<4, 2>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide_causal<2, 2>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_wide_causal<1, 3>(const DecodeParams&, hipStream_t);
 
 }  // namespace mla355

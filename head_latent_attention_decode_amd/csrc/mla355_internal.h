@@ -84,6 +84,9 @@ struct DecodeParams {
     // [b, t_max, 576] and cache_scale [b, t_max] the per-token scales
     const float* cache_scale;
     int num_blocks, block_size, max_blocks;
+    // several causal query tokens per row (causal kernels only): the h
+    // "heads" are q_len tokens x heads_per_token heads
+    int q_len, heads_per_token;
     int b, h, t_max;
     int n_chunks;         // chunks per head group
     int n_hg;             // head groups
@@ -119,6 +122,10 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int va
 // Wide-wave bf16 kernel: NW waves of 32 heads each, STAGES-deep LDS ring.
 template <int NW, int STAGES>
 hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
+
+// The same with q_len causal query tokens per row (p.q_len, p.heads_per_token).
+template <int NW, int STAGES>
+hipError_t launch_decode_wide_causal(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
 

@@ -188,6 +188,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t*
     for (int s = lane; s < ns; s += 64) m = fmaxf(m, pl[(size_t)s * h]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (m == -INFINITY) {
+        // no segment saw a token (a causal query row with an empty prefix)
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = 0.f;
+        store8(out + ((size_t)r * h + head) * kDc + 8 * lane, z);
+        if (lane == 0) lse[(size_t)r * h + head] = -INFINITY;
+        return;
+    }
     float sm = 0.f;
     for (int s = lane; s < ns; s += 64) sm += expf(pl[(size_t)s * h] - m);
 #pragma unroll

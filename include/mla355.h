@@ -154,6 +154,40 @@ mla_status_t mla_decode_ex(mla_dtype_t dtype, int b, int h, int t_max, const voi
 const char* mla_decode_kernel_name(mla_dtype_t dtype, int h, const mla_decode_config_t* config);
 
 /*
+ * mla_decode_mtp -- mla_decode with q_len new query tokens per batch row
+ * (several tokens decoded at once, e.g. speculative or multi-token
+ * prediction steps).  The glossary's production notes say prefill and decode
+ * take different paths; the Polish overview gives attention's cost over
+ * every (token, earlier token) pair.  Neither spells out a mask; the reading
+ * taken here is the standard causal one: the q_len new tokens are the last
+ * q_len of the L = seqlens[i] cached rows of row i (already appended), and new
+ * token n (0-based) attends to the first L - q_len + 1 + n rows, its own
+ * included.  For each (i, n, j):
+ *   s_t = softmax_scale * q_prime[i,n,j,:] . cache[i,t,:],  t < L - q_len + 1 + n
+ *   out[i,n,j,:] = sum_t softmax(s)_t cache[i,t,0:512],  lse[i,n,j] = log sum_t exp(s_t)
+ * A token with no row to attend to (L < q_len - n) gets out = 0, lse = -inf.
+ * q_len = 1 is exactly mla_decode (same kernels, same results).
+ * Layouts: q_prime [b,q_len,h,576] bf16; cache [b,t_max,576] bf16; seqlens [b]
+ * int32 on the device, clamped to [0, t_max]; out [b,q_len,h,512] bf16
+ * (written); lse [b,q_len,h] fp32 (written).
+ * workspace: device scratch of at least mla_decode_mtp_workspace_bytes(...)
+ * bytes, 256-byte aligned, contents need not be initialised.
+ * Errors (host side, before any launch): MLA_ERR_UNSUPPORTED for dtype
+ * MLA_DTYPE_F32; MLA_ERR_INVALID_ARGUMENT for an unknown dtype, a null or
+ * misaligned pointer, b <= 0, q_len <= 0, h <= 0, q_len*h > 2^20, t_max < 0,
+ * b*t_max >= 2^31, or softmax_scale not finite or <= 0;
+ * MLA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t mla_decode_mtp_workspace_bytes(mla_dtype_t dtype, int b, int q_len, int h, int t_max);
+mla_status_t mla_decode_mtp(mla_dtype_t dtype, int b, int q_len, int h, int t_max,
+                            const void* q_prime, const void* cache, const int32_t* seqlens,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+/* Name of the attention kernel mla_decode_mtp launches (pure host function;
+ * NULL for arguments it would reject). */
+const char* mla_decode_mtp_kernel_name(mla_dtype_t dtype, int q_len, int h);
+
+/*
  * mla_decode_paged -- mla_decode over a paged latent cache.  The cached rows
  * of every sequence live in fixed-size blocks of a shared pool, found through
  * a block table (glossary, capacity and cost section: MLA leaves dynamic

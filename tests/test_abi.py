@@ -199,3 +199,44 @@ def test_fp8_validation_and_queries(mla):
     # two resident workgroups per CU: twice the chunks of the bf16 schedule
     assert mla.mla_decode_fp8_workspace_bytes(128, 16, 8192) == \
         mla.mla_decode_workspace_bytes(torch.bfloat16, 128, 16, 8192, {"n_chunks": 512})
+
+
+def _decode_mtp(lib, dt=1, b=2, ql=2, h=16, t=100, q=A, c=A, sl=A, scale=SCALE, out=A, lse=A, ws=A,
+                wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_decode_mtp(dt, b, ql, h, t, vp(q), vp(c), vp(sl), ctypes.c_float(scale), vp(out),
+                              vp(lse), vp(ws), ctypes.c_size_t(wsb), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dt": 0}, 2), ({"dt": 5}, 1), ({"ql": 0}, 1), ({"ql": -3}, 1), ({"ql": 1 << 20}, 1),
+    ({"b": 0}, 1), ({"h": 0}, 1), ({"t": -1}, 1), ({"q": 0}, 1), ({"c": 0}, 1), ({"sl": 0}, 1),
+    ({"out": 0}, 1), ({"lse": 0}, 1), ({"ws": 0}, 1), ({"q": A + 8}, 1), ({"lse": A + 4}, 1),
+    ({"ws": A + 16}, 1), ({"scale": 0.0}, 1), ({"scale": float("nan")}, 1), ({"wsb": 1024}, 3),
+    ({"b": 1 << 20, "t": 1 << 12}, 1),
+    # one query token: the same validation as mla_decode
+    ({"ql": 1, "q": 0}, 1), ({"ql": 1, "scale": -1.0}, 1), ({"ql": 1, "wsb": 1024}, 3),
+])
+def test_decode_mtp_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _decode_mtp(lib, **kw) == status
+
+
+def test_decode_mtp_host_queries(mla):
+    # query rows = q_len * h; 32 per wave, up to 4 waves per workgroup
+    assert mla.mla_decode_mtp_kernel_name(2, 128) == "decode_wide_causal_kernel<4, 2, false>"
+    assert mla.mla_decode_mtp_kernel_name(3, 16) == "decode_wide_causal_kernel<2, 2, false>"
+    assert mla.mla_decode_mtp_kernel_name(2, 16) == "decode_wide_causal_kernel<1, 3, false>"
+    assert mla.mla_decode_mtp_kernel_name(1, 128) == mla.mla_decode_kernel_name(torch.bfloat16, 128)
+    assert mla.mla_decode_mtp_kernel_name(0, 128) is None
+    assert mla.mla_decode_mtp_kernel_name(1 << 14, 128) is None
+    # one token: exactly mla_decode's workspace; more: that of q_len*h heads
+    assert mla.mla_decode_mtp_workspace_bytes(64, 1, 128, 4096) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
+    assert mla.mla_decode_mtp_workspace_bytes(64, 2, 128, 4096) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 256, 4096,
+                                       {"heads_per_group": 128, "n_chunks": 128})
+    assert mla.mla_decode_mtp_workspace_bytes(64, 0, 128, 4096) == 0
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    lib.mla_decode_mtp_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.mla_decode_mtp_workspace_bytes(0, 4, 2, 16, 100) == 0  # fp32 has no causal form

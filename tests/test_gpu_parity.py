@@ -427,3 +427,75 @@ def test_full_long_context_end_to_end(mla):
                                       w.seqlens.cpu(), w.scale)
     ref_y = oracle.absorb_o(ref_out, w.w_uv.cpu()[heads])
     assert_out(to_np(y[:, heads]), ref_y, BF16_OUT_REL, "y")
+
+
+# ---- several causal query tokens per row (mla_decode_mtp) ---------------------
+
+MTP_CASES = [
+    # (q_len, h, lengths)
+    (2, 128, [700, 257, 1000, 33, 2]),   # 256 query rows: two groups of 128
+    (3, 16, [100, 3, 1, 0, 64]),         # 48 rows; lengths below q_len and an empty row
+    (4, 8, [129, 32, 31, 5]),            # 32 rows
+    (2, 100, [513, 96]),                 # 200 rows, the last group padded
+    (8, 16, [300, 40, 8]),               # 128 rows, a row of exactly q_len
+]
+
+
+def _mtp_workload(b, q_len, h, lens, seed):
+    w = workloads.make_custom(b, q_len * h, lens, seed=seed, device="cuda")
+    return w, w.q_prime.view(b, q_len, h, 576)
+
+
+@pytest.mark.parametrize("q_len,h,lens", MTP_CASES, ids=["q%d-h%d" % (c[0], c[1]) for c in MTP_CASES])
+def test_mtp_every_output(mla, q_len, h, lens):
+    b = len(lens)
+    w, q = _mtp_workload(b, q_len, h, lens, seed=700 + q_len * h)
+    out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode_latent_causal(q.cpu(), w.cache.cpu(), w.seqlens.cpu().numpy(), w.scale)
+    assert_out(to_np(out), ref_o, BF16_OUT_REL)
+    assert_lse(to_np(lse), ref_l, BF16_LSE_ABS)
+    # tokens with nothing to attend to: exactly zero output
+    n = np.clip(np.array(lens)[:, None] - q_len + 1 + np.arange(q_len)[None, :], 0, None)
+    for i in range(b):
+        for t in range(q_len):
+            if n[i, t] == 0:
+                assert torch.all(out[i, t] == 0) and torch.all(torch.isneginf(lse[i, t]))
+
+
+def test_mtp_one_token_is_decode(mla):
+    w = workloads.make_custom(3, 128, [400, 1, 77], seed=81, device="cuda")
+    q = w.q_prime.view(3, 1, 128, 576)
+    out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
+    out_d, lse_d = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(3, 128, 512), out_d) and torch.equal(lse.view(3, 128), lse_d)
+
+
+def test_mtp_token_matches_decode_of_its_prefix(mla):
+    # new token i of a row equals plain decode of the same query over the
+    # first L - q_len + 1 + i rows (both within tolerance of the oracle, and
+    # of each other)
+    b, q_len, h = 2, 4, 64
+    lens = [900, 130]
+    w, q = _mtp_workload(b, q_len, h, lens, seed=82)
+    out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
+    for i in range(q_len):
+        sl = torch.tensor([L - q_len + 1 + i for L in lens], dtype=torch.int32, device="cuda")
+        od, ld = mla.mla_decode(q[:, i].contiguous(), w.cache, sl, w.scale)
+        assert_out(to_np(out[:, i]), to_np(od), BF16_OUT_REL)
+        assert_lse(to_np(lse[:, i]), to_np(ld), BF16_LSE_ABS)
+
+
+def test_full_dsv3_decode_mtp2_b64_h128_T4096(mla):
+    # the 128-head configuration with two query tokens per row; sampled rows
+    b, q_len, h, T = 64, 2, 128, 4096
+    w = workloads.make_custom(b, q_len * h, [T] * b, seed=83, device="cuda", poison=False)
+    q = w.q_prime.view(b, q_len, h, 576)
+    out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    rows = [0, 37, 63]
+    ref_o, ref_l = oracle.decode_latent_causal(q[rows].cpu(), w.cache[rows].cpu(),
+                                               w.seqlens[rows].cpu().numpy(), w.scale)
+    assert_out(to_np(out[rows]), ref_o, BF16_OUT_REL)
+    assert_lse(to_np(lse[rows]), ref_l, BF16_LSE_ABS)
