@@ -51,15 +51,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work_counts(b, h, lens, elt=2):
-    """Algorithmic FLOPs and bytes of each step stage."""
+def work_counts(b, h, lens, elt=2, q_len=1):
+    """Algorithmic FLOPs and bytes of each step stage.  With q_len causal query
+    tokens per row, new token i of a row of L cached rows scores the first
+    L - q_len + 1 + i of them; the cache is still read once per row."""
     sum_l = int(sum(lens))
-    dec_flop = 2 * (D_QK + D_C) * h * sum_l
-    dec_bytes = sum_l * D_QK * elt + b * h * (D_QK * elt + D_C * elt + 4)
-    aq_flop = 2 * b * h * D_K * D_C
-    aq_bytes = b * h * (D_K + D_R + D_QK) * elt + h * D_K * D_C * elt
-    ao_flop = 2 * b * h * D_C * D_V
-    ao_bytes = b * h * (D_C + D_V) * elt + h * D_C * D_V * elt
+    visible = sum(min(max(int(L) - q_len + 1 + i, 0), int(L)) for L in lens for i in range(q_len))
+    nq = b * q_len  # query tokens
+    dec_flop = 2 * (D_QK + D_C) * h * visible
+    dec_bytes = sum_l * D_QK * elt + nq * h * (D_QK * elt + D_C * elt + 4)
+    aq_flop = 2 * nq * h * D_K * D_C
+    aq_bytes = nq * h * (D_K + D_R + D_QK) * elt + h * D_K * D_C * elt
+    ao_flop = 2 * nq * h * D_C * D_V
+    ao_bytes = nq * h * (D_C + D_V) * elt + h * D_C * D_V * elt
     return {"decode": (dec_flop, dec_bytes), "absorb_q": (aq_flop, aq_bytes),
             "absorb_o": (ao_flop, ao_bytes)}
 
@@ -110,38 +114,47 @@ def load_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None):
+def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None, q_len=1):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workload: whole batch rows, all heads, absorb -> latent decode -> absorb."""
+    workload: whole batch rows, all heads (and query tokens), absorb -> latent
+    decode -> absorb."""
     import numpy as np
     import oracle
     orc = oracle.default()
     lens = w.seqlens.cpu().tolist()
     wk = w_uk.cpu()
     wv = w_uv.cpu()
+    qn_all = q_nope.view(w.b, q_len, w.h, -1)
+    qr_all = q_rope.view(w.b, q_len, w.h, -1)
 
     def run(rows):
         L = max(int(lens[r]) for r in rows)
-        qn, qr = q_nope[rows].cpu(), q_rope[rows].cpu()
+        n = len(rows)
+        qn = qn_all[rows].reshape(n * q_len, w.h, -1).cpu()
+        qr = qr_all[rows].reshape(n * q_len, w.h, -1).cpu()
         c = w.cache[rows, :L].cpu()
         sl = np.array([lens[r] for r in rows], np.int32)
         cf = oracle._f64(c)  # widen outside the timed region
         t0 = time.perf_counter()
         qp = orc.absorb_q(qn, wk, qr)
-        out, _ = orc.decode_latent(qp, cf, sl, w.scale)
-        orc.absorb_o(out, wv)
+        if q_len == 1:
+            out, _ = orc.decode_latent(qp, cf, sl, w.scale)
+        else:
+            out, _ = orc.decode_latent_causal(qp.reshape(n, q_len, w.h, -1), cf, sl, w.scale)
+        orc.absorb_o(out.reshape(n * q_len, w.h, -1), wv)
         dt = time.perf_counter() - t0
-        cnt = work_counts(len(rows), w.h, [lens[r] for r in rows])
+        cnt = work_counts(n, w.h, [lens[r] for r in rows], q_len=q_len)
         return dt, sum(f for f, _ in cnt.values())
 
     dt1, f1 = run([0])
     n = int(min(w.b if max_rows is None else max_rows, max(1, round(target_s / max(dt1, 1e-3)))))
     rows = list(range(n))
     dt, fl = run(rows)
+    toks = "" if q_len == 1 else " x %d query tokens" % q_len
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
             "kind": "oracle",
-            "sample": "%d of %d batch rows, all %d heads, %d cached tokens each: fp64 absorb_q -> "
-                      "latent-form decode -> absorb_o, %.1f s" % (n, w.b, w.h, lens[0], dt)}
+            "sample": "%d of %d batch rows%s, all %d heads, %d cached tokens each: fp64 absorb_q -> "
+                      "latent-form decode -> absorb_o, %.1f s" % (n, w.b, toks, w.h, lens[0], dt)}
 
 
 PROFILE_CMDS = {
@@ -273,6 +286,9 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="read the cache through a paged pool of BLOCK-token blocks (shuffled "
                          "block table) with mla_decode_paged")
+    ap.add_argument("--q-len", type=int, default=1, metavar="N",
+                    help="N causal query tokens per batch row (the last N cached rows), decoded "
+                         "with mla_decode_mtp")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and exit: "
                          "the reference for scaling HBM traffic counters")
@@ -333,6 +349,22 @@ def main():
     if args.fp8 and args.paged:
         print("--fp8 and --paged cannot be combined", file=sys.stderr)
         sys.exit(2)
+    q_len = args.q_len
+    mtp = None
+    if q_len > 1:
+        if args.fp8 or args.paged or args.hpg or args.variant:
+            print("--q-len takes neither --fp8, --paged, --hpg nor --variant", file=sys.stderr)
+            sys.exit(2)
+        # q-side tensors for b * q_len query tokens (same heads and weights)
+        q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(w.b * q_len, w.h, dtype=w.dtype,
+                                                                 device="cuda")
+        mtp = {"q_prime": torch.empty((w.b * q_len, w.h, D_QK), dtype=w.dtype, device=dev),
+               "out": torch.empty((w.b, q_len, w.h, D_C), dtype=w.dtype, device=dev),
+               "lse": torch.empty((w.b, q_len, w.h), dtype=torch.float32, device=dev),
+               "y": torch.empty((w.b * q_len, w.h, D_V), dtype=w.dtype, device=dev),
+               "ws": torch.empty(mla.mla_decode_mtp_workspace_bytes(w.b, q_len, w.h, w.t_max,
+                                                                   sched or None),
+                                 dtype=torch.uint8, device=dev)}
     if args.fp8:
         codes, scales = mla.mla_quantize_cache_fp8(w.cache)
         need = mla.mla_decode_fp8_workspace_bytes(w.b, w.h, w.t_max, sched or None)
@@ -369,7 +401,12 @@ def main():
         c = dict(sched)
         if i is not None:
             c["profile_events"] = (ev[i][1].value, ev[i][2].value)
-        if codes is not None:
+        if mtp is not None:
+            mla.mla_absorb_q(q_nope, w_uk, q_rope, mtp["q_prime"])
+            mla.mla_decode_mtp(mtp["q_prime"].view(w.b, q_len, w.h, D_QK), w.cache, w.seqlens,
+                               w.scale, mtp["out"], mtp["lse"], mtp["ws"], config=c or None)
+            mla.mla_absorb_o(mtp["out"].view(w.b * q_len, w.h, D_C), w_uv, mtp["y"])
+        elif codes is not None:
             mla.mla_absorb_q(q_nope, w_uk, q_rope, bufs.q_prime)
             mla.mla_decode_fp8(bufs.q_prime, codes, scales, w.seqlens, w.scale, bufs.out, bufs.lse,
                                bufs.workspace, config=c or None)
@@ -410,7 +447,7 @@ def main():
     torch.cuda.synchronize()
     b2b_ms = hip.elapsed_ms(b0, b1) / K
 
-    cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize)
+    cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize, q_len=q_len)
     if args.fp8:
         # the cache streams 576 code bytes + a 4-byte scale per token
         f, _ = cnt["decode"]
@@ -423,7 +460,9 @@ def main():
     value = step_flop / (ms * 1e-3) / 1e12
     k_gbs = dec_bytes / (kms * 1e-3) / 1e9
     k_tfl = dec_flop / (kms * 1e-3) / 1e12
-    traffic = None if (args.paged or args.fp8) else load_traffic(cfg.name)
+    traffic = None if (args.paged or args.fp8 or mtp is not None) else load_traffic(cfg.name)
+    # the roof the attention kernel meets first: HBM bytes or MFMA FLOPs
+    mfma_bound = dec_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12) > dec_bytes / (HBM_PEAK_GBS * 1e9)
     log("step: mean %.2f us (min %.2f, max %.2f); split-KV kernel mean %.2f us (min %.2f); "
         "back-to-back step %.2f us; wall %.3f s for %d steps" %
         (ms * 1e3, min(step_ms) * 1e3, max(step_ms) * 1e3, kms * 1e3, min(kern_ms) * 1e3,
@@ -446,18 +485,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": w.b, "heads": w.h, "cached_tokens": w.t_max,
                    "sum_cached_tokens": int(sum(lens)), "d_latent": D_C, "d_rope": D_R,
-                   "step": "absorb_q + decode (plan, split-KV, combine) + absorb_o",
+                   "step": ("absorb_q + decode (plan, split-KV, combine) + absorb_o" if q_len == 1 else
+                            "absorb_q + causal multi-token decode (plan, split-KV, combine) + absorb_o"),
                    "cache_evicted_between_steps": flush is not None,
                    "schedule": sched or "auto",
                    "cache_layout": ("paged, %d-token blocks, shuffled block table" % args.paged
                                     if args.paged else "contiguous"),
-                   "cache_dtype": "e4m3 codes + fp32 per-token scale" if args.fp8 else str(w.dtype)},
+                   "cache_dtype": "e4m3 codes + fp32 per-token scale" if args.fp8 else str(w.dtype),
+                   "query_tokens_per_row": q_len},
         "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_flop": step_flop,
         "step_bytes": step_bytes,
         "ms_per_step_back_to_back": round(b2b_ms, 5),
         "roofline": {"kernel": (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
                                 else mla.mla_decode_fp8_kernel_name(w.h, sched or None) if args.fp8
+                                else mla.mla_decode_mtp_kernel_name(q_len, w.h) if mtp is not None
                                 else mla.mla_decode_kernel_name(w.dtype, w.h, sched or None)),
                      "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
@@ -466,9 +508,19 @@ def main():
         "mfma": {"achieved": round(k_tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(k_tfl / MFMA_BF16_PEAK_TFLOPS, 4), "alg_flop_per_launch": dec_flop},
     }
+    if mfma_bound:
+        # compute-bound shape: the roofline object reports the MFMA roof, the
+        # byte rate moves to the secondary object
+        r = res["roofline"]
+        res["hbm"] = {k: r[k] for k in ("achieved", "peak", "unit", "frac", "alg_bytes_per_launch")}
+        r.update({"bound": "mfma", "achieved": round(k_tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(k_tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "alg_flop_per_launch": dec_flop})
+        del r["alg_bytes_per_launch"]
+        del res["mfma"]
     if not args.no_cpu_baseline:
         t_c = time.perf_counter()
-        res["cpu_baseline"] = cpu_baseline(w, q_nope, q_rope, w_uk, w_uv)
+        res["cpu_baseline"] = cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, q_len=q_len)
         log("cpu baseline %.1f s" % (time.perf_counter() - t_c))
     print(json.dumps(res), flush=True)
 

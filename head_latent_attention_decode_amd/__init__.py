@@ -92,6 +92,11 @@ _lib.mla_decode_mtp_kernel_name.restype = ctypes.c_char_p
 _lib.mla_decode_mtp_kernel_name.argtypes = [_ci, _ci, _ci]
 _lib.mla_decode_mtp.restype = _ci
 _lib.mla_decode_mtp.argtypes = [_ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
+_lib.mla_decode_mtp_workspace_bytes_ex.restype = _sz
+_lib.mla_decode_mtp_workspace_bytes_ex.argtypes = [_ci, _ci, _ci, _ci, _ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_mtp_ex.restype = _ci
+_lib.mla_decode_mtp_ex.argtypes = [_ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
+                                   ctypes.POINTER(MLAConfig), _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
@@ -99,7 +104,8 @@ EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla
                     "mla_decode_paged", "mla_decode_paged_ex", "mla_decode_paged_kernel_name",
                     "mla_quantize_cache_fp8", "mla_decode_fp8_workspace_bytes", "mla_decode_fp8",
                     "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name",
-                    "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name")
+                    "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name",
+                    "mla_decode_mtp_workspace_bytes_ex", "mla_decode_mtp_ex")
 
 
 class MLAError(RuntimeError):
@@ -245,13 +251,13 @@ def mla_decode_mtp_kernel_name(q_len: int, h: int):
     return None if name is None else name.decode()
 
 
-def mla_decode_mtp_workspace_bytes(b: int, q_len: int, h: int, t_max: int) -> int:
+def mla_decode_mtp_workspace_bytes(b: int, q_len: int, h: int, t_max: int, config=None) -> int:
     """Bytes of workspace mla_decode_mtp needs (pure host computation, no GPU)."""
-    return int(_lib.mla_decode_mtp_workspace_bytes(MLA_DTYPE_BF16, b, q_len, h, t_max))
+    return int(_lib.mla_decode_mtp_workspace_bytes_ex(MLA_DTYPE_BF16, b, q_len, h, t_max, _cfg(config)))
 
 
 def mla_decode_mtp(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, workspace=None,
-                   stream=None):
+                   config=None, stream=None):
     """Latent-form decode of q_len causal query tokens per row (bf16).
 
     q_prime [b,q_len,h,576], cache [b,t_max,576], seqlens [b] int32 on the GPU
@@ -268,14 +274,14 @@ def mla_decode_mtp(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, w
         out = torch.empty((b, q_len, h, D_C), dtype=dt, device=dev)
     if lse is None:
         lse = torch.empty((b, q_len, h), dtype=torch.float32, device=dev)
-    need = mla_decode_mtp_workspace_bytes(b, q_len, h, t_max)
+    need = mla_decode_mtp_workspace_bytes(b, q_len, h, t_max, config)
     if need == 0:
-        raise ValueError("invalid problem: b=%d q_len=%d h=%d t_max=%d" % (b, q_len, h, t_max))
+        raise ValueError("invalid problem or config: b=%d q_len=%d h=%d t_max=%d" % (b, q_len, h, t_max))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
         raise TypeError("workspace must be a uint8 GPU tensor")
-    st = _lib.mla_decode_mtp(MLA_DTYPE_BF16, b, q_len, h, t_max,
+    st = _lib.mla_decode_mtp_ex(MLA_DTYPE_BF16, b, q_len, h, t_max,
                              _dev(q_prime, "q_prime", (b, q_len, h, D_QK), dt),
                              _dev(cache, "cache", (b, t_max, D_QK), dt),
                              _dev(seqlens, "seqlens", (b,), torch.int32),
@@ -283,7 +289,7 @@ def mla_decode_mtp(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, w
                              _dev(out, "out", (b, q_len, h, D_C), dt),
                              _dev(lse, "lse", (b, q_len, h), torch.float32),
                              ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
-                             _stream(stream))
+                             _cfg(config), _stream(stream))
     _check(st, "mla_decode_mtp")
     return out, lse
 

@@ -259,12 +259,39 @@ bool mtp_dims_ok(int b, int q_len, int h, int t_max)
     return dims_ok(b, q_len * h, t_max);
 }
 
-size_t mla_decode_mtp_workspace_bytes(mla_dtype_t dt, int b, int q_len, int h, int t_max)
+// Config of the multi-token call: only n_chunks and the profiling events may be set.
+mla_status_t check_mtp_config(const mla_decode_config_t* cfg)
+{
+    if (!cfg) return MLA_OK;
+    for (int i = 0; i < 5; ++i)
+        if (cfg->reserved[i] != 0) return MLA_ERR_UNSUPPORTED;
+    if (cfg->heads_per_group != 0 || cfg->variant != 0) return MLA_ERR_UNSUPPORTED;
+    if (cfg->n_chunks < 0 || cfg->n_chunks % 8 != 0 || cfg->n_chunks > kMaxChunks) return MLA_ERR_UNSUPPORTED;
+    if ((cfg->profile_events[0] == nullptr) != (cfg->profile_events[1] == nullptr))
+        return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+MtpSchedule mtp_schedule(int rows, const mla_decode_config_t* cfg)
+{
+    MtpSchedule s = choose_mtp_schedule(rows);
+    if (cfg && cfg->n_chunks != 0) s.n_chunks = cfg->n_chunks;
+    return s;
+}
+
+size_t mla_decode_mtp_workspace_bytes_ex(mla_dtype_t dt, int b, int q_len, int h, int t_max,
+                                         const mla_decode_config_t* cfg)
 {
     if (dt != MLA_DTYPE_BF16 || !mtp_dims_ok(b, q_len, h, t_max)) return 0;
-    if (q_len == 1) return mla_decode_workspace_bytes(dt, b, h, t_max);
-    const MtpSchedule s = choose_mtp_schedule(q_len * h);
+    if (check_mtp_config(cfg) != MLA_OK) return 0;
+    if (q_len == 1) return mla_decode_workspace_bytes_ex(dt, b, h, t_max, cfg);
+    const MtpSchedule s = mtp_schedule(q_len * h, cfg);
     return workspace_layout(b, q_len * h, s.n_chunks, 2).total;
+}
+
+size_t mla_decode_mtp_workspace_bytes(mla_dtype_t dt, int b, int q_len, int h, int t_max)
+{
+    return mla_decode_mtp_workspace_bytes_ex(dt, b, q_len, h, t_max, nullptr);
 }
 
 const char* mla_decode_mtp_kernel_name(mla_dtype_t dt, int q_len, int h)
@@ -279,24 +306,26 @@ const char* mla_decode_mtp_kernel_name(mla_dtype_t dt, int q_len, int h)
     }
 }
 
-mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, const void* q_prime,
-                            const void* cache, const int32_t* seqlens, float softmax_scale,
-                            void* out, float* lse, void* workspace, size_t workspace_bytes,
-                            void* stream)
+mla_status_t mla_decode_mtp_ex(mla_dtype_t dt, int b, int q_len, int h, int t_max,
+                               const void* q_prime, const void* cache, const int32_t* seqlens,
+                               float softmax_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, const mla_decode_config_t* cfg, void* stream)
 {
     if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
     if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
     if (!mtp_dims_ok(b, q_len, h, t_max)) return MLA_ERR_INVALID_ARGUMENT;
+    const mla_status_t cst = check_mtp_config(cfg);
+    if (cst != MLA_OK) return cst;
     if (q_len == 1)
         return mla_decode_ex(dt, b, h, t_max, q_prime, cache, seqlens, softmax_scale, out, lse,
-                             workspace, workspace_bytes, nullptr, stream);
+                             workspace, workspace_bytes, cfg, stream);
     if (!q_prime || !cache || !seqlens || !out || !lse || !workspace) return MLA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q_prime) || !aligned16(cache) || !aligned16(seqlens) || !aligned16(out) ||
         !aligned16(lse) || ((uintptr_t)workspace & 255u) != 0)
         return MLA_ERR_INVALID_ARGUMENT;
     if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
     const int rows = q_len * h;
-    const MtpSchedule s = choose_mtp_schedule(rows);
+    const MtpSchedule s = mtp_schedule(rows, cfg);
     const WorkspaceLayout w = workspace_layout(b, rows, s.n_chunks, 2);
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -324,14 +353,27 @@ mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, 
     p.n_hg = s.n_hg;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
 
+    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
+    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
     hipError_t e = launch_plan(seqlens, b, rows, t_max, s.n_chunks, 32, 1, plan, true, out, lse, hs);
     if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
     e = s.nw == 4   ? launch_decode_wide_causal<4, 2>(p, hs)
         : s.nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
                     : launch_decode_wide_causal<1, 3>(p, hs);
     if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
     e = launch_combine(true, plan, b, rows, p.plse, p.po, out, lse, hs);
     return hip_status(e);
+}
+
+mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, const void* q_prime,
+                            const void* cache, const int32_t* seqlens, float softmax_scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream)
+{
+    return mla_decode_mtp_ex(dt, b, q_len, h, t_max, q_prime, cache, seqlens, softmax_scale, out,
+                             lse, workspace, workspace_bytes, nullptr, stream);
 }
 
 size_t mla_decode_paged_workspace_bytes(mla_dtype_t dt, int b, int h, int num_blocks,

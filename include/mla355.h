@@ -183,6 +183,17 @@ mla_status_t mla_decode_mtp(mla_dtype_t dtype, int b, int q_len, int h, int t_ma
                             const void* q_prime, const void* cache, const int32_t* seqlens,
                             float softmax_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+/* As mla_decode_mtp_workspace_bytes / mla_decode_mtp with a config (may be
+ * NULL): only n_chunks (the split count, a multiple of 8, 0 = automatic) and
+ * profile_events may be set; any other field non-zero, or an n_chunks outside
+ * its range, gives MLA_ERR_UNSUPPORTED (workspace query: 0). */
+size_t mla_decode_mtp_workspace_bytes_ex(mla_dtype_t dtype, int b, int q_len, int h, int t_max,
+                                         const mla_decode_config_t* config);
+mla_status_t mla_decode_mtp_ex(mla_dtype_t dtype, int b, int q_len, int h, int t_max,
+                               const void* q_prime, const void* cache, const int32_t* seqlens,
+                               float softmax_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, const mla_decode_config_t* config,
+                               void* stream);
 /* Name of the attention kernel mla_decode_mtp launches (pure host function;
  * NULL for arguments it would reject). */
 const char* mla_decode_mtp_kernel_name(mla_dtype_t dtype, int q_len, int h);

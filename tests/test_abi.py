@@ -240,3 +240,24 @@ def test_decode_mtp_host_queries(mla):
     lib = ctypes.CDLL(mla.LIB_PATH)
     lib.mla_decode_mtp_workspace_bytes.restype = ctypes.c_size_t
     assert lib.mla_decode_mtp_workspace_bytes(0, 4, 2, 16, 100) == 0  # fp32 has no causal form
+
+
+def test_decode_mtp_ex_config(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.mla_decode_mtp_workspace_bytes_ex.restype = ctypes.c_size_t
+    for cfg in ({"n_chunks": 12}, {"n_chunks": -8}, {"heads_per_group": 128}, {"variant": 1},
+                {"reserved": (ctypes.c_int * 5)(0, 0, 1, 0, 0)}):
+        c = mla.MLAConfig()
+        for k, v in cfg.items():
+            setattr(c, k, v)
+        for ql in (1, 2):
+            st = lib.mla_decode_mtp_ex(1, 2, ql, 16, 100, vp(A), vp(A), vp(A), ctypes.c_float(SCALE),
+                                       vp(A), vp(A), vp(A), ctypes.c_size_t(1 << 30), ctypes.byref(c),
+                                       vp(0))
+            assert st == 2, (cfg, ql)
+            assert lib.mla_decode_mtp_workspace_bytes_ex(1, 2, ql, 16, 100, ctypes.byref(c)) == 0
+    # a split count of its own changes the workspace like mla_decode_ex's does
+    assert mla.mla_decode_mtp_workspace_bytes(64, 2, 128, 4096, {"n_chunks": 256}) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 256, 4096,
+                                       {"heads_per_group": 128, "n_chunks": 256})
