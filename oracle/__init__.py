@@ -91,6 +91,8 @@ class Oracle:
         lib.oracle_decode_unabsorbed.argtypes = [ci, ci, ci, ci, ci, ci, ci, dp, dp, dp, dp,
                                                  dp, ip, cd, ip, ci, dp, dp, dp, dp]
         lib.oracle_decode_unabsorbed.restype = None
+        lib.oracle_cache_append.argtypes = [ci, ci, ci, ci, ci, ci, dp, dp, dp, dp, dp, ip, dp]
+        lib.oracle_cache_append.restype = None
         lib.oracle_absorb_q.argtypes = [ci, ci, ci, ci, ci, dp, dp, dp, dp]
         lib.oracle_absorb_q.restype = None
         lib.oracle_absorb_o.argtypes = [ci, ci, ci, ci, dp, dp, dp]
@@ -172,6 +174,23 @@ class Oracle:
                                           _ip(hs), n_sel, _dp(y), _dp(lse), _dp(sc), _dp(pr))
         return (y, lse, sc, pr) if want_scores else (y, lse)
 
+    def cache_append(self, x, w_dkv, w_kr, cos_tab, sin_tab, seqlens, cache):
+        """Write the new token's latent row [x W_DKV ; RoPE(x W_KR)] into row
+        seqlens[i] of each batch row.  x [b,d_model], w_dkv [d_model,d_c],
+        w_kr [d_model,d_r], cos_tab/sin_tab [n_pos,d_r/2], cache [b,t_max,d_c+d_r].
+        Returns the updated cache (a new fp64 array)."""
+        xx, wd, wr, ct, st = (_f64(a) for a in (x, w_dkv, w_kr, cos_tab, sin_tab))
+        c = _f64(cache).copy()
+        sl = _i32(seqlens)
+        b, d_model = xx.shape
+        d_c, d_r = wd.shape[1], wr.shape[1]
+        n_pos = ct.shape[0]
+        assert wd.shape[0] == d_model and wr.shape[0] == d_model and st.shape == ct.shape
+        assert ct.shape[1] == d_r // 2 and c.shape[0] == b and c.shape[2] == d_c + d_r
+        self.lib.oracle_cache_append(b, d_model, d_c, d_r, c.shape[1], n_pos, _dp(xx), _dp(wd),
+                                     _dp(wr), _dp(ct), _dp(st), _ip(sl), _dp(c))
+        return c
+
     def absorb_q(self, q_nope, w_uk, q_rope):
         """q'[b,h,:d_c] = q_nope[b,h,:] @ w_uk[h] ; q'[b,h,d_c:] = q_rope[b,h,:]."""
         qn, wk, qr = _f64(q_nope), _f64(w_uk), _f64(q_rope)
@@ -214,6 +233,10 @@ def decode_unabsorbed(*a, **k):
 
 def decode_latent_causal(*a, **k):
     return default().decode_latent_causal(*a, **k)
+
+
+def cache_append(*a, **k):
+    return default().cache_append(*a, **k)
 
 
 def absorb_q(*a, **k):

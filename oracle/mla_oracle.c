@@ -245,6 +245,52 @@ void oracle_decode_latent_causal(int b, int q_len, int h, int t_max, int d_c, in
 }
 
 /*
+ * Appending the new token's latent row (the step before attention).
+ * Glossary "Multi-head Latent Attention", layout difference from MHA/GQA: the
+ * cached content part is c_t = x_t W^DKV and the cached RoPE key is
+ * k^R_t = RoPE(x_t W^KR), one per token, shared by all heads; Lesson 28 shows
+ * the hidden state (width d_model, e.g. 7168) down-projected to the 512-wide
+ * latent that is cached.  The pages fix no RoPE base or pairing; reading: the
+ * caller supplies the rotation as tables cos_tab/sin_tab [n_pos, d_r/2] and
+ * RoPE turns each adjacent pair (2j, 2j+1) of x W^KR by the angle of entry
+ * (pos, j):
+ *   k[2j]   = r[2j] cos - r[2j+1] sin,   k[2j+1] = r[2j] sin + r[2j+1] cos.
+ * The new token of batch row i is written at row pos = seqlens[i] (its
+ * position); a row with pos outside [0, min(t_max, n_pos)) is not written.
+ * x [b, d_model], w_dkv [d_model, d_c], w_kr [d_model, d_r], cache
+ * [b, t_max, d_c + d_r] (updated in place).
+ */
+void oracle_cache_append(int b, int d_model, int d_c, int d_r, int t_max, int n_pos,
+                         const double* x, const double* w_dkv, const double* w_kr,
+                         const double* cos_tab, const double* sin_tab,
+                         const int32_t* seqlens, double* cache)
+{
+    const int d = d_c + d_r;
+#pragma omp parallel for schedule(static)
+    for (int bi = 0; bi < b; ++bi) {
+        const int pos = seqlens[bi];
+        if (pos < 0 || pos >= t_max || pos >= n_pos) continue;
+        const double* xr = x + IDX2(bi, 0, d_model);
+        double* row = cache + IDX3(bi, pos, 0, t_max, d);
+        for (int c = 0; c < d_c; ++c) {
+            double acc = 0.0;
+            for (int k = 0; k < d_model; ++k) acc += xr[k] * w_dkv[IDX2(k, c, d_c)];
+            row[c] = acc;
+        }
+        for (int j = 0; j < d_r / 2; ++j) {
+            double r0 = 0.0, r1 = 0.0;
+            for (int k = 0; k < d_model; ++k) {
+                r0 += xr[k] * w_kr[IDX2(k, 2 * j, d_r)];
+                r1 += xr[k] * w_kr[IDX2(k, 2 * j + 1, d_r)];
+            }
+            const double cs = cos_tab[IDX2(pos, j, d_r / 2)], sn = sin_tab[IDX2(pos, j, d_r / 2)];
+            row[d_c + 2 * j] = r0 * cs - r1 * sn;
+            row[d_c + 2 * j + 1] = r0 * sn + r1 * cs;
+        }
+    }
+}
+
+/*
  * Query absorption: q'[b,h,0:d_c] = q_nope[b,h,:] (W^UK_h)^T and
  * q'[b,h,d_c:d_c+d_r] = q_rope[b,h,:].
  * Glossary "Multi-head Latent Attention", why decode absorbs: qbar_h =

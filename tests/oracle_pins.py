@@ -398,6 +398,71 @@ def pin_causal_future_rows_unseen(orc, seed=26):
                 assert np.all(np.isnan(out[0, qi])), "token %d must see row of token %d" % (qi, j)
 
 
+def _rope_tables(n_pos, half, base=10000.0):
+    """Rotation tables of the RoFormer form: angle pos * base^(-j/half)."""
+    ang = np.arange(n_pos)[:, None] * base ** (-np.arange(half)[None, :] / half)
+    return np.cos(ang), np.sin(ang)
+
+
+def pin_append_projection_vs_matmul(orc, seed=27):
+    """Identity rotation (cos = 1, sin = 0): the appended row is exactly
+    [x W_DKV ; x W_KR] (numpy matmul), written at row seqlens[i] only."""
+    g = _rng(seed)
+    b, d_model, t_max = 3, 40, 9
+    x = g.standard_normal((b, d_model))
+    wd = g.standard_normal((d_model, 512))
+    wr = g.standard_normal((d_model, 64))
+    cache = g.standard_normal((b, t_max, 576))
+    lens = np.array([0, 5, 8], np.int32)
+    out = orc.cache_append(x, wd, wr, np.ones((t_max, 32)), np.zeros((t_max, 32)), lens, cache)
+    for i in range(b):
+        ref = np.concatenate([x[i] @ wd, x[i] @ wr])
+        _close(out[i, lens[i]], ref, 1e-12, "appended row = [x W_DKV ; x W_KR]")
+        keep = np.ones(t_max, bool)
+        keep[lens[i]] = False
+        assert np.array_equal(out[i, keep], cache[i, keep]), "other rows untouched"
+
+
+def pin_append_rope_properties(orc, seed=28):
+    """RoPE as rotations: each pair keeps its length, the content part does not
+    move, and the dot product of two keys rotated at positions m and n depends
+    only on m - n (shift both rows by 5 positions: same dot product)."""
+    g = _rng(seed)
+    d_model, t_max = 16, 40
+    cos_t, sin_t = _rope_tables(t_max, 32)
+    x = g.standard_normal((2, d_model))
+    wd = g.standard_normal((d_model, 512))
+    wr = g.standard_normal((d_model, 64))
+    cache = np.zeros((2, t_max, 576))
+    ident = orc.cache_append(x, wd, wr, np.ones((t_max, 32)), np.zeros((t_max, 32)),
+                             np.array([3, 11], np.int32), cache)
+    rot = orc.cache_append(x, wd, wr, cos_t, sin_t, np.array([3, 11], np.int32), cache)
+    for i, pos in enumerate((3, 11)):
+        _close(rot[i, pos, :512], ident[i, pos, :512], 0.0, "content part not rotated")
+        r = ident[i, pos, 512:].reshape(32, 2)
+        k = rot[i, pos, 512:].reshape(32, 2)
+        _close(np.hypot(k[:, 0], k[:, 1]), np.hypot(r[:, 0], r[:, 1]), 1e-12, "pair length kept")
+    shifted = orc.cache_append(x, wd, wr, cos_t, sin_t, np.array([8, 16], np.int32), cache)
+    d0 = rot[0, 3, 512:] @ rot[1, 11, 512:]
+    d1 = shifted[0, 8, 512:] @ shifted[1, 16, 512:]
+    _close(np.array([d1]), np.array([d0]), 1e-10, "relative-position dot product")
+    # the rotation itself, position 3 of pair 0 written out
+    r0, r1 = ident[0, 3, 512], ident[0, 3, 513]
+    _close(np.array([rot[0, 3, 512], rot[0, 3, 513]]),
+           np.array([r0 * math.cos(3.0) - r1 * math.sin(3.0), r0 * math.sin(3.0) + r1 * math.cos(3.0)]),
+           1e-12, "pair 0 turned by its angle")
+
+
+def pin_append_out_of_range_rows(orc, seed=29):
+    """A length at or past the cache (or the tables) or negative writes nothing."""
+    g = _rng(seed)
+    x = g.standard_normal((3, 8))
+    cache = g.standard_normal((3, 6, 576))
+    out = orc.cache_append(x, g.standard_normal((8, 512)), g.standard_normal((8, 64)),
+                           np.ones((5, 32)), np.zeros((5, 32)), np.array([6, -1, 5], np.int32), cache)
+    assert np.array_equal(out, cache)
+
+
 ALL_PINS = [
     pin_glossary_toy_identities,
     pin_identities_c1_dims,
@@ -416,4 +481,7 @@ ALL_PINS = [
     pin_causal_vs_sdpa,
     pin_causal_zero_query,
     pin_causal_future_rows_unseen,
+    pin_append_projection_vs_matmul,
+    pin_append_rope_properties,
+    pin_append_out_of_range_rows,
 ]

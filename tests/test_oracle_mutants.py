@@ -32,6 +32,13 @@ MUTANTS = [
     ("causal_limit_off_by_one", "int n = L - q_len + 1 + qi;", "int n = L - q_len + qi;", 0),
     ("causal_no_mask", "int n = L - q_len + 1 + qi;", "int n = L;", 0),
     ("causal_reversed_tokens", "int n = L - q_len + 1 + qi;", "int n = L - qi;", 0),
+    ("append_rope_sign", "row[d_c + 2 * j] = r0 * cs - r1 * sn;", "row[d_c + 2 * j] = r0 * cs + r1 * sn;", 0),
+    ("append_rope_pairs_swapped", "row[d_c + 2 * j + 1] = r0 * sn + r1 * cs;",
+     "row[d_c + 2 * j + 1] = r1 * sn + r0 * cs;", 0),
+    ("append_wrong_row", "double* row = cache + IDX3(bi, pos, 0, t_max, d);",
+     "double* row = cache + IDX3(bi, pos > 0 ? pos - 1 : 0, 0, t_max, d);", 0),
+    ("append_wrong_table_row", "const double cs = cos_tab[IDX2(pos, j, d_r / 2)]",
+     "const double cs = cos_tab[IDX2(0, j, d_r / 2)]", 0),
 ]
 
 
