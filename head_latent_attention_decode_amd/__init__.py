@@ -97,6 +97,11 @@ _lib.mla_decode_mtp_workspace_bytes_ex.argtypes = [_ci, _ci, _ci, _ci, _ci, ctyp
 _lib.mla_decode_mtp_ex.restype = _ci
 _lib.mla_decode_mtp_ex.argtypes = [_ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
                                    ctypes.POINTER(MLAConfig), _vp]
+_lib.mla_cache_append_workspace_bytes.restype = _sz
+_lib.mla_cache_append_workspace_bytes.argtypes = [_ci, _ci]
+_lib.mla_cache_append.restype = _ci
+_lib.mla_cache_append.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _vp, _vp, _ci, _vp, _vp, _vp, _vp,
+                                  _sz, _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
@@ -105,7 +110,8 @@ EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla
                     "mla_quantize_cache_fp8", "mla_decode_fp8_workspace_bytes", "mla_decode_fp8",
                     "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name",
                     "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name",
-                    "mla_decode_mtp_workspace_bytes_ex", "mla_decode_mtp_ex")
+                    "mla_decode_mtp_workspace_bytes_ex", "mla_decode_mtp_ex",
+                    "mla_cache_append_workspace_bytes", "mla_cache_append")
 
 
 class MLAError(RuntimeError):
@@ -292,6 +298,46 @@ def mla_decode_mtp(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, w
                              _cfg(config), _stream(stream))
     _check(st, "mla_decode_mtp")
     return out, lse
+
+
+def mla_cache_append_workspace_bytes(b: int, d_model: int) -> int:
+    """Bytes of workspace mla_cache_append needs (pure host computation, no GPU)."""
+    return int(_lib.mla_cache_append_workspace_bytes(b, d_model))
+
+
+def mla_cache_append(x, w_dkv, w_kr, rope_cos, rope_sin, cache, seqlens, seqlens_out=None,
+                     workspace=None, stream=None):
+    """Write [x W_DKV ; RoPE(x W_KR)] (bf16) into row seqlens[i] of each batch row.
+
+    x [b,d_model], w_dkv [d_model,512], w_kr [d_model,64] bf16; rope_cos /
+    rope_sin [n_pos,32] fp32; cache [b,t_max,576] bf16 (updated in place);
+    seqlens [b] int32; seqlens_out: optional int32 [b] (may be seqlens itself)
+    that receives the lengths including the new token.  Returns cache.
+    """
+    b, d_model = x.shape
+    t_max = cache.shape[1]
+    n_pos = rope_cos.shape[0]
+    dev = x.device
+    need = mla_cache_append_workspace_bytes(b, d_model)
+    if need == 0:
+        raise ValueError("invalid append problem: b=%d d_model=%d" % (b, d_model))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    so = None if seqlens_out is None else _dev(seqlens_out, "seqlens_out", (b,), torch.int32)
+    st = _lib.mla_cache_append(MLA_DTYPE_BF16, b, d_model, t_max,
+                               _dev(x, "x", (b, d_model), torch.bfloat16),
+                               _dev(w_dkv, "w_dkv", (d_model, D_C), torch.bfloat16),
+                               _dev(w_kr, "w_kr", (d_model, D_R), torch.bfloat16),
+                               _dev(rope_cos, "rope_cos", (n_pos, D_R // 2), torch.float32),
+                               _dev(rope_sin, "rope_sin", (n_pos, D_R // 2), torch.float32), n_pos,
+                               _dev(cache, "cache", (b, t_max, D_QK), torch.bfloat16),
+                               _dev(seqlens, "seqlens", (b,), torch.int32), so,
+                               ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                               _stream(stream))
+    _check(st, "mla_cache_append")
+    return cache
 
 
 def mla_decode_paged_kernel_name(h: int, config=None):

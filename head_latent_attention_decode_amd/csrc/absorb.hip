@@ -147,11 +147,13 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
 // with ds_read_b64_tr_b16); batch rows are the B columns, 16 per block.  When
 // rope != nullptr (q absorb), the workgroups of column block 0 also copy
 // rope[m][h][0:64] to y[...][ND:ND+64].
-template <int KD, int ND, int NCB>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __bf16* __restrict__ x,
-                                                          long x_rs, const __bf16* __restrict__ w,
-                                                          __bf16* __restrict__ y, long y_rs, int y_hs,
-                                                          const __bf16* __restrict__ rope)
+// blk: this workgroup's index among the product's H * ND / (64 NCB) blocks;
+// OutT: type of Y (bf16, or fp32 for partial sums that are added up later).
+template <int KD, int ND, int NCB, typename OutT>
+__device__ __forceinline__ void absorb_mfma_body(int blk, int M, int H, const __bf16* __restrict__ x,
+                                                 long x_rs, const __bf16* __restrict__ w,
+                                                 OutT* __restrict__ y, long y_rs, int y_hs,
+                                                 const __bf16* __restrict__ rope)
 {
     constexpr int NB = ND / (64 * NCB);       // workgroups per head
     constexpr int KSTEPS = KD / 32;
@@ -165,8 +167,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __
     static_assert(X_ROW >= 256, "16 chunks per staged row for the swizzle");
     lds_byte* slab = stage_lds<W_BYTES, 0>();
     lds_byte* xs = stage_lds<X_BYTES, 1>();
-    const int h = blockIdx.x / NB;
-    const int n0 = (blockIdx.x % NB) * 64 * NCB;
+    const int h = blk / NB;
+    const int n0 = (blk % NB) * 64 * NCB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -257,16 +259,96 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __
                 // acc[i]: output column n0 + 64cb + 16*wave + g*4 + i of batch row m
                 const int m = mb0 * 64 + mb * 16 + s;
                 if (m < M) {
-                    bf16x4_t o;
-                    o[0] = (__bf16)acc[0];
-                    o[1] = (__bf16)acc[1];
-                    o[2] = (__bf16)acc[2];
-                    o[3] = (__bf16)acc[3];
-                    *(bf16x4_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + cb * 64 + wave * 16 + g * 4) = o;
+                    OutT* dst = y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + cb * 64 + wave * 16 + g * 4;
+                    if constexpr (sizeof(OutT) == 2) {
+                        bf16x4_t o;
+                        o[0] = (__bf16)acc[0];
+                        o[1] = (__bf16)acc[1];
+                        o[2] = (__bf16)acc[2];
+                        o[3] = (__bf16)acc[3];
+                        *(bf16x4_t*)dst = o;
+                    } else {
+                        *(f32x4_t*)dst = acc;
+                    }
                 }
             }
         }
     }
+}
+
+template <int KD, int ND, int NCB>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __bf16* __restrict__ x,
+                                                          long x_rs, const __bf16* __restrict__ w,
+                                                          __bf16* __restrict__ y, long y_rs, int y_hs,
+                                                          const __bf16* __restrict__ rope)
+{
+    absorb_mfma_body<KD, ND, NCB, __bf16>(blockIdx.x, M, H, x, x_rs, w, y, y_rs, y_hs, rope);
+}
+
+// ---- appending a token's latent row ------------------------------------------
+// Glossary "Multi-head Latent Attention", layout difference from MHA/GQA: the
+// cached row of token t is [c_t ; k^R_t] with c_t = x_t W^DKV (d_c = 512) and
+// k^R_t = RoPE(x_t W^KR) (d_r = 64); Lesson 28: x_t is the d_model-wide
+// hidden state (7168 in its example).  The projection is the per-head product
+// above with the hidden dimension cut into d_model / kAppendKD chunks taking
+// the place of heads: chunk h of every x row times rows h*kAppendKD.. of
+// W_DKV (512 columns, 8 blocks of 64) and of W_KR (64 columns, 1 block), into
+// fp32 partial sums P[m][h][0:576].  One launch covers both weights.
+constexpr int kAppendKD = 256;
+
+__global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __bf16* __restrict__ x,
+                                                          const __bf16* __restrict__ w_dkv,
+                                                          const __bf16* __restrict__ w_kr,
+                                                          float* __restrict__ part)
+{
+    const long x_rs = (long)H * kAppendKD;
+    const int dkv_blocks = H * (kDc / 64);
+    if ((int)blockIdx.x < dkv_blocks)
+        absorb_mfma_body<kAppendKD, kDc, 1, float>(blockIdx.x, M, H, x, x_rs, w_dkv, part,
+                                                   (long)H * kDqk, kDqk, nullptr);
+    else
+        absorb_mfma_body<kAppendKD, kDr, 1, float>(blockIdx.x - dkv_blocks, M, H, x, x_rs, w_kr,
+                                                   part + kDc, (long)H * kDqk, kDqk, nullptr);
+}
+
+// One workgroup per batch row: sum the H partials of the 576 columns, turn
+// each adjacent pair (2j, 2j+1) of the 64 RoPE columns by the table entry of
+// the row's position pos = seqlens[m], and write the bf16 row at cache row
+// pos (nothing when pos is outside [0, min(t_max, n_pos))).  seqlens_out (may
+// be null or equal to seqlens) gets pos + 1 for a written row, pos otherwise.
+__global__ __launch_bounds__(256) void append_finish_kernel(int H, int t_max, int n_pos,
+                                                            const float* __restrict__ part,
+                                                            const float* __restrict__ rope_cos,
+                                                            const float* __restrict__ rope_sin,
+                                                            __bf16* __restrict__ cache,
+                                                            const int32_t* seqlens, int32_t* seqlens_out)
+{
+    __shared__ float row[kDqk];
+    const int m = blockIdx.x;
+    const int t = threadIdx.x;
+    const int pos = seqlens[m];
+    const bool write = pos >= 0 && pos < t_max && pos < n_pos;
+    if (write) {
+        const float* pm = part + (size_t)m * H * kDqk;
+        for (int c = t; c < kDqk; c += 256) {
+            float acc = 0.f;
+            for (int h = 0; h < H; ++h) acc += pm[(size_t)h * kDqk + c];
+            row[c] = acc;
+        }
+    }
+    __syncthreads();  // every thread has read seqlens[m] before it may be overwritten
+    if (write) {
+        __bf16* dst = cache + ((size_t)m * t_max + pos) * kDqk;
+        for (int c = t; c < kDc; c += 256) dst[c] = (__bf16)row[c];
+        if (t < kDr / 2) {
+            const float cs = rope_cos[(size_t)pos * (kDr / 2) + t];
+            const float sn = rope_sin[(size_t)pos * (kDr / 2) + t];
+            const float r0 = row[kDc + 2 * t], r1 = row[kDc + 2 * t + 1];
+            dst[kDc + 2 * t] = (__bf16)(r0 * cs - r1 * sn);
+            dst[kDc + 2 * t + 1] = (__bf16)(r0 * sn + r1 * cs);
+        }
+    }
+    if (seqlens_out != nullptr && t == 0) seqlens_out[m] = write ? pos + 1 : pos;
 }
 
 constexpr int kAbsorbQSlabs = 4;  // 64-column weight slabs per q-absorb workgroup
@@ -285,6 +367,28 @@ hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const vo
         absorb_q_kernel<float><<<grid, 128, 0, stream>>>(b, h, (const float*)q_nope,
                                                          (const float*)w_uk, (const float*)q_rope,
                                                          (float*)q_prime);
+    return hipGetLastError();
+}
+
+size_t append_workspace_bytes(int b, int d_model)
+{
+    return (size_t)b * (size_t)(d_model / kAppendKD) * kDqk * sizeof(float);
+}
+
+int append_kd() { return kAppendKD; }
+
+hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
+                               const void* w_dkv, const void* w_kr, const float* rope_cos,
+                               const float* rope_sin, void* cache, const int32_t* seqlens,
+                               int32_t* seqlens_out, float* part, hipStream_t stream)
+{
+    const int H = d_model / kAppendKD;
+    append_proj_kernel<<<H * (kDc / 64 + 1), 256, 0, stream>>>(b, H, (const __bf16*)x, (const __bf16*)w_dkv,
+                                                               (const __bf16*)w_kr, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    append_finish_kernel<<<b, 256, 0, stream>>>(H, t_max, n_pos, part, rope_cos, rope_sin, (__bf16*)cache,
+                                                seqlens, seqlens_out);
     return hipGetLastError();
 }
 

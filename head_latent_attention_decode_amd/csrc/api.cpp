@@ -569,6 +569,37 @@ mla_status_t mla_absorb_q(mla_dtype_t dt, int b, int h, const void* q_nope, cons
                                       (hipStream_t)stream));
 }
 
+size_t mla_cache_append_workspace_bytes(int b, int d_model)
+{
+    if (b <= 0 || d_model <= 0 || d_model % append_kd() != 0) return 0;
+    return align_up(append_workspace_bytes(b, d_model), 256);
+}
+
+mla_status_t mla_cache_append(mla_dtype_t dt, int b, int d_model, int t_max, const void* x,
+                              const void* w_dkv, const void* w_kr, const float* rope_cos,
+                              const float* rope_sin, int n_pos, void* cache, const int32_t* seqlens,
+                              int32_t* seqlens_out, void* workspace, size_t workspace_bytes,
+                              void* stream)
+{
+    if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
+    if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+    if (b <= 0 || d_model <= 0 || d_model % append_kd() != 0 || t_max <= 0 || n_pos <= 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)b * t_max >= ((int64_t)1 << 31) || (int64_t)b * d_model >= ((int64_t)1 << 31))
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!x || !w_dkv || !w_kr || !rope_cos || !rope_sin || !cache || !seqlens || !workspace)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(cache) ||
+        ((uintptr_t)rope_cos & 3u) != 0 || ((uintptr_t)rope_sin & 3u) != 0 ||
+        ((uintptr_t)seqlens & 3u) != 0 || ((uintptr_t)seqlens_out & 3u) != 0 ||
+        ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < mla_cache_append_workspace_bytes(b, d_model)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_cache_append(b, d_model, t_max, n_pos, x, w_dkv, w_kr, rope_cos, rope_sin,
+                                          cache, seqlens, seqlens_out, (float*)workspace,
+                                          (hipStream_t)stream));
+}
+
 mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,
                           void* stream)
 {

@@ -199,6 +199,40 @@ mla_status_t mla_decode_mtp_ex(mla_dtype_t dtype, int b, int q_len, int h, int t
 const char* mla_decode_mtp_kernel_name(mla_dtype_t dtype, int q_len, int h);
 
 /*
+ * mla_cache_append -- write the new token's latent row into the cache (the
+ * step before attention).  Glossary "Multi-head Latent Attention", layout
+ * difference from MHA/GQA: the cached row of token t is [c_t ; k^R_t] with
+ * c_t = x_t W^DKV and k^R_t = RoPE(x_t W^KR), one RoPE key shared by all heads;
+ * Lesson 28 ("Down-projection and On-the-Fly Up-projection in MLA"): x_t is the
+ * d_model-wide hidden state (7168 in its example).  The pages give no RoPE base
+ * or pairing: the caller supplies the rotation as tables rope_cos/rope_sin
+ * [n_pos, 32] (fp32, entry (p, j) = cos/sin of the angle of pair j at position
+ * p), and RoPE turns each adjacent pair (2j, 2j+1) of x W^KR:
+ *   k[2j] = r[2j] cos - r[2j+1] sin,   k[2j+1] = r[2j] sin + r[2j+1] cos.
+ * Batch row i's token goes to cache row pos = seqlens[i] (its position), in
+ * bf16 after fp32 accumulation; a row with pos outside [0, min(t_max, n_pos))
+ * is not written.  seqlens_out (may be NULL, may equal seqlens) receives pos + 1
+ * for a written row and pos otherwise, so that the following attention call
+ * sees the new token.
+ * Layouts: x [b, d_model] bf16; w_dkv [d_model, 512] bf16; w_kr [d_model, 64]
+ * bf16 (row-major); cache [b, t_max, 576] bf16 (updated in place).
+ * workspace: device scratch of at least mla_cache_append_workspace_bytes(b,
+ * d_model) bytes (fp32 partial sums), 256-byte aligned.
+ * Errors (host side, before any launch): MLA_ERR_UNSUPPORTED for dtype
+ * MLA_DTYPE_F32; MLA_ERR_INVALID_ARGUMENT for an unknown dtype, a null pointer
+ * (seqlens_out excepted), x / w_dkv / w_kr / cache not 16-byte aligned, the
+ * tables or seqlens not 4-byte aligned, b <= 0, t_max <= 0, n_pos <= 0, d_model
+ * not a positive multiple of 256, b*t_max >= 2^31 or b*d_model >= 2^31;
+ * MLA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t mla_cache_append_workspace_bytes(int b, int d_model);
+mla_status_t mla_cache_append(mla_dtype_t dtype, int b, int d_model, int t_max, const void* x,
+                              const void* w_dkv, const void* w_kr, const float* rope_cos,
+                              const float* rope_sin, int n_pos, void* cache, const int32_t* seqlens,
+                              int32_t* seqlens_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * mla_decode_paged -- mla_decode over a paged latent cache.  The cached rows
  * of every sequence live in fixed-size blocks of a shared pool, found through
  * a block table (glossary, capacity and cost section: MLA leaves dynamic

@@ -261,3 +261,32 @@ def test_decode_mtp_ex_config(mla):
     assert mla.mla_decode_mtp_workspace_bytes(64, 2, 128, 4096, {"n_chunks": 256}) == \
         mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 256, 4096,
                                        {"heads_per_group": 128, "n_chunks": 256})
+
+
+def _append(lib, dt=1, b=4, dm=512, t=64, x=A, wd=A, wr=A, cs=A, sn=A, npos=64, c=A, sl=A, so=0,
+            ws=A, wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_cache_append(dt, b, dm, t, vp(x), vp(wd), vp(wr), vp(cs), vp(sn), npos, vp(c), vp(sl),
+                                vp(so), vp(ws), ctypes.c_size_t(wsb), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dt": 0}, 2), ({"dt": 4}, 1), ({"b": 0}, 1), ({"dm": 0}, 1), ({"dm": 100}, 1), ({"dm": 384}, 1),
+    ({"t": 0}, 1), ({"npos": 0}, 1), ({"x": 0}, 1), ({"wd": 0}, 1), ({"wr": 0}, 1), ({"cs": 0}, 1),
+    ({"sn": 0}, 1), ({"c": 0}, 1), ({"sl": 0}, 1), ({"ws": 0}, 1), ({"x": A + 8}, 1), ({"wr": A + 4}, 1),
+    ({"c": A + 2}, 1), ({"cs": A + 2}, 1), ({"sl": A + 2}, 1), ({"so": A + 1}, 1), ({"ws": A + 16}, 1),
+    ({"wsb": 1024}, 3), ({"b": 1 << 20, "t": 1 << 12}, 1),
+])
+def test_cache_append_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _append(lib, **kw) == status
+
+
+def test_cache_append_workspace(mla):
+    # fp32 partial sums: one 576-wide row per batch row and 256-wide hidden chunk
+    assert mla.mla_cache_append_workspace_bytes(64, 7168) == 64 * 28 * 576 * 4
+    assert mla.mla_cache_append_workspace_bytes(3, 256) == 3 * 576 * 4  # a multiple of 256 already
+    assert mla.mla_cache_append_workspace_bytes(1, 256) == 2304
+    assert mla.mla_cache_append_workspace_bytes(5, 256) == -(-5 * 576 * 4 // 256) * 256
+    assert mla.mla_cache_append_workspace_bytes(64, 7000) == 0
+    assert mla.mla_cache_append_workspace_bytes(0, 7168) == 0

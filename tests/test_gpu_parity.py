@@ -499,3 +499,97 @@ def test_full_dsv3_decode_mtp2_b64_h128_T4096(mla):
                                                w.seqlens[rows].cpu().numpy(), w.scale)
     assert_out(to_np(out[rows]), ref_o, BF16_OUT_REL)
     assert_lse(to_np(lse[rows]), ref_l, BF16_LSE_ABS)
+
+
+# ---- appending a token's latent row (mla_cache_append) ------------------------
+
+def _append_inputs(b, d_model, t_max, n_pos, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(b, d_model, generator=g).to(torch.bfloat16)
+    wd = (torch.randn(d_model, 512, generator=g) / math.sqrt(d_model)).to(torch.bfloat16)
+    wr = (torch.randn(d_model, 64, generator=g) / math.sqrt(d_model)).to(torch.bfloat16)
+    cache = torch.randn(b, t_max, 576, generator=g).to(torch.bfloat16)
+    # caller-chosen rotation tables (RoFormer-style angles, base 10000)
+    ang = np.arange(n_pos)[:, None] * 10000.0 ** (-np.arange(32)[None, :] / 32.0)
+    cos_t = torch.from_numpy(np.cos(ang).astype(np.float32))
+    sin_t = torch.from_numpy(np.sin(ang).astype(np.float32))
+    return [t.cuda() for t in (x, wd, wr, cos_t, sin_t, cache)]
+
+
+def _check_append(before, after, ref, lens, t_max, n_pos):
+    written = [(i, L) for i, L in enumerate(lens) if 0 <= L < min(t_max, n_pos)]
+    got = np.stack([to_np(after[i, L]) for i, L in written])
+    want = np.stack([ref[i, L] for i, L in written])
+    assert_out(got, want, BF16_OUT_REL, "appended rows")
+    mask = torch.ones(after.shape[:2], dtype=torch.bool, device=after.device)
+    for i, L in written:
+        mask[i, L] = False
+    assert torch.equal(after[mask], before[mask]), "rows other than the appended ones changed"
+
+
+@pytest.mark.parametrize("d_model", [256, 7168])
+def test_cache_append_every_row(mla, d_model):
+    lens = [0, 7, 47, 48, -3, 20]
+    b, t_max, n_pos = len(lens), 48, 48
+    x, wd, wr, cos_t, sin_t, cache = _append_inputs(b, d_model, t_max, n_pos, seed=90 + d_model)
+    before = cache.clone()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sl_out = torch.empty_like(sl)
+    mla.mla_cache_append(x, wd, wr, cos_t, sin_t, cache, sl, sl_out)
+    torch.cuda.synchronize()
+    ref = oracle.cache_append(x.cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(), np.array(lens, np.int32),
+                              before.cpu())
+    _check_append(before, cache, ref, lens, t_max, n_pos)
+    assert sl_out.cpu().tolist() == [1, 8, 48, 48, -3, 21]
+    assert sl.cpu().tolist() == lens
+
+
+def test_cache_append_in_place_lengths_and_table_bound(mla):
+    # seqlens updated in place; a position past the tables (n_pos < t_max) is not written
+    lens = [3, 10, 9]
+    b, t_max, n_pos = 3, 16, 10
+    x, wd, wr, cos_t, sin_t, cache = _append_inputs(b, 512, t_max, n_pos, seed=95)
+    before = cache.clone()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    mla.mla_cache_append(x, wd, wr, cos_t, sin_t, cache, sl, sl)
+    torch.cuda.synchronize()
+    ref = oracle.cache_append(x.cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(), np.array(lens, np.int32),
+                              before.cpu())
+    _check_append(before, cache, ref, lens, t_max, n_pos)
+    assert sl.cpu().tolist() == [4, 10, 10]
+
+
+def test_cache_append_then_decode(mla):
+    # one decode step: append the new token, then attend with it included
+    b, h, d_model, t_max = 4, 128, 7168, 600
+    lens = [599, 0, 257, 31]
+    x, wd, wr, cos_t, sin_t, cache = _append_inputs(b, d_model, t_max, t_max, seed=96)
+    before = cache.clone()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    mla.mla_cache_append(x, wd, wr, cos_t, sin_t, cache, sl, sl)
+    g = torch.Generator().manual_seed(97)
+    q = torch.randn(b, h, 576, generator=g).to(torch.bfloat16).cuda()
+    out, lse = mla.mla_decode(q, cache, sl, 1.0 / math.sqrt(192.0))
+    torch.cuda.synchronize()
+    ref = oracle.cache_append(x.cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(), np.array(lens, np.int32),
+                              before.cpu())
+    _check_append(before, cache, ref, lens, t_max, t_max)
+    # attention over the cache as the GPU wrote it (the appended row included)
+    check_decode(q, cache, sl, 1.0 / math.sqrt(192.0), out, lse, range(b))
+
+
+def test_cache_append_dsv3_b64(mla):
+    # the hidden width of the glossary's example (7168), 64 rows at position 4095
+    b, d_model, t_max = 64, 7168, 4096
+    x, wd, wr, cos_t, sin_t, cache = _append_inputs(b, d_model, t_max, t_max, seed=98)
+    before = cache.clone()
+    lens = [4095] * b
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    mla.mla_cache_append(x, wd, wr, cos_t, sin_t, cache, sl)
+    torch.cuda.synchronize()
+    rows = [0, 33, 63]
+    ref = oracle.cache_append(x[rows].cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(),
+                              np.array([4095] * 3, np.int32), before[rows].cpu())
+    got = np.stack([to_np(cache[r, 4095]) for r in rows])
+    assert_out(got, ref[:, 4095], BF16_OUT_REL, "appended rows")
+    assert torch.equal(cache[:, :4095], before[:, :4095])
