@@ -269,6 +269,62 @@ def workloads_counts(workload):
     raise SystemExit("no fixed-length workload named %s" % workload)
 
 
+def bench_append(args, torch, mla, workloads, dev):
+    """Time mla_cache_append alone: b rows of hidden width d_model projected to
+    [x W_DKV ; RoPE(x W_KR)] and written at row t_max - 1 of the config's cache."""
+    import numpy as np
+    cfg = workloads.CONFIGS[args.config]
+    w = workloads.make(args.config, device="cuda", poison=False)
+    d_model = args.append
+    g = torch.Generator().manual_seed(4243)
+    x = torch.randn(w.b, d_model, generator=g).to(torch.bfloat16).to(dev)
+    wd = (torch.randn(d_model, D_C, generator=g) / d_model ** 0.5).to(torch.bfloat16).to(dev)
+    wr = (torch.randn(d_model, D_R, generator=g) / d_model ** 0.5).to(torch.bfloat16).to(dev)
+    ang = np.arange(w.t_max)[:, None] * 10000.0 ** (-np.arange(D_R // 2)[None, :] / (D_R // 2))
+    cos_t = torch.from_numpy(np.cos(ang).astype(np.float32)).to(dev)
+    sin_t = torch.from_numpy(np.sin(ang).astype(np.float32)).to(dev)
+    pos = torch.full((w.b,), w.t_max - 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(mla.mla_cache_append_workspace_bytes(w.b, d_model), dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    ev = [[hip.event() for _ in range(2)] for _ in range(K)]
+
+    def step():
+        mla.mla_cache_append(x, wd, wr, cos_t, sin_t, w.cache, pos, workspace=ws)
+
+    for _ in range(W):
+        if flush is not None:
+            flush.sum()
+        step()
+    torch.cuda.synchronize()
+    for i in range(K):
+        if flush is not None:
+            flush.sum()
+        hip.record(ev[i][0], stream)
+        step()
+        hip.record(ev[i][1], stream)
+    torch.cuda.synchronize()
+    ms = sum(hip.elapsed_ms(e[0], e[1]) for e in ev) / K
+    flop = 2 * w.b * d_model * D_QK
+    byts = d_model * D_QK * 2 + w.b * d_model * 2 + w.b * (D_QK * 2 + 4)  # weights, x, rows
+    gbs = byts / (ms * 1e-3) / 1e9
+    res = {"metric": "MLA cache append GB/s (% of roofline)", "value": round(gbs, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name + "_append_d%d" % d_model, "batch": w.b, "d_model": d_model,
+                      "step": "mla_cache_append (projection, RoPE, row write)",
+                      "cache_evicted_between_steps": flush is not None},
+           "roofline": {"kernel": "append_proj_kernel + append_finish_kernel", "bound": "hbm",
+                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "launch_us": round(ms * 1e3, 2), "alg_bytes_per_launch": byts},
+           "mfma": {"achieved": round(flop / (ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "alg_flop_per_launch": flop}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +345,9 @@ def main():
     ap.add_argument("--q-len", type=int, default=1, metavar="N",
                     help="N causal query tokens per batch row (the last N cached rows), decoded "
                          "with mla_decode_mtp")
+    ap.add_argument("--append", type=int, default=0, metavar="D_MODEL",
+                    help="time mla_cache_append alone (hidden width D_MODEL, one new row per batch "
+                         "row of the configuration) instead of the decode step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and exit: "
                          "the reference for scaling HBM traffic counters")
@@ -326,6 +385,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.append:
+        bench_append(args, torch, mla, workloads, dev)
         return
     cfg = workloads.CONFIGS[args.config]
     t_setup = time.perf_counter()

@@ -299,8 +299,12 @@ constexpr int kAppendKD = 256;
 __global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __bf16* __restrict__ x,
                                                           const __bf16* __restrict__ w_dkv,
                                                           const __bf16* __restrict__ w_kr,
-                                                          float* __restrict__ part)
+                                                          float* __restrict__ part,
+                                                          const int32_t* __restrict__ seqlens,
+                                                          int32_t* __restrict__ wpos)
 {
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < M; i += 256) wpos[i] = seqlens[i];
     const long x_rs = (long)H * kAppendKD;
     const int dkv_blocks = H * (kDc / 64);
     if ((int)blockIdx.x < dkv_blocks)
@@ -311,44 +315,60 @@ __global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __
                                                    part + kDc, (long)H * kDqk, kDqk, nullptr);
 }
 
-// One workgroup per batch row: sum the H partials of the 576 columns, turn
-// each adjacent pair (2j, 2j+1) of the 64 RoPE columns by the table entry of
-// the row's position pos = seqlens[m], and write the bf16 row at cache row
-// pos (nothing when pos is outside [0, min(t_max, n_pos))).  seqlens_out (may
-// be null or equal to seqlens) gets pos + 1 for a written row, pos otherwise.
+// One workgroup per (batch row m, block of 64 of the 576 columns): sum the H
+// partials of its columns (thread t: column t % 64, every fourth chunk from
+// t / 64, loads issued eight at a time), then write them as bf16 at cache row
+// pos; the block of the 64 RoPE columns first turns each adjacent pair (2j,
+// 2j+1) by the table entry (pos, j).  pos is the copy of seqlens[m] the
+// projection kernel took (so that an in-place length update by block 0 cannot
+// race with the other blocks' reads); nothing is written when pos is outside
+// [0, min(t_max, n_pos)).  Block 0 writes seqlens_out[m] (may be null or equal
+// to seqlens): pos + 1 for a written row, pos otherwise.
 __global__ __launch_bounds__(256) void append_finish_kernel(int H, int t_max, int n_pos,
                                                             const float* __restrict__ part,
+                                                            const int32_t* __restrict__ wpos,
                                                             const float* __restrict__ rope_cos,
                                                             const float* __restrict__ rope_sin,
                                                             __bf16* __restrict__ cache,
-                                                            const int32_t* seqlens, int32_t* seqlens_out)
+                                                            int32_t* seqlens_out)
 {
-    __shared__ float row[kDqk];
-    const int m = blockIdx.x;
+    __shared__ float red[4][64];
+    constexpr int NCB = kDqk / 64;
+    const int m = blockIdx.x / NCB, cb = blockIdx.x % NCB;
     const int t = threadIdx.x;
-    const int pos = seqlens[m];
+    const int pos = wpos[m];
     const bool write = pos >= 0 && pos < t_max && pos < n_pos;
-    if (write) {
-        const float* pm = part + (size_t)m * H * kDqk;
-        for (int c = t; c < kDqk; c += 256) {
-            float acc = 0.f;
-            for (int h = 0; h < H; ++h) acc += pm[(size_t)h * kDqk + c];
-            row[c] = acc;
+    if (cb == 0 && t == 0 && seqlens_out != nullptr) seqlens_out[m] = write ? pos + 1 : pos;
+    if (!write) return;
+    const int col = cb * 64 + (t & 63);
+    const float* pm = part + (size_t)m * H * kDqk + col;
+    float acc = 0.f;
+    for (int h0 = t >> 6; h0 < H; h0 += 32) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int h = h0 + 4 * u;
+            v[u] = h < H ? pm[(size_t)h * kDqk] : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
     }
-    __syncthreads();  // every thread has read seqlens[m] before it may be overwritten
-    if (write) {
-        __bf16* dst = cache + ((size_t)m * t_max + pos) * kDqk;
-        for (int c = t; c < kDc; c += 256) dst[c] = (__bf16)row[c];
-        if (t < kDr / 2) {
-            const float cs = rope_cos[(size_t)pos * (kDr / 2) + t];
-            const float sn = rope_sin[(size_t)pos * (kDr / 2) + t];
-            const float r0 = row[kDc + 2 * t], r1 = row[kDc + 2 * t + 1];
-            dst[kDc + 2 * t] = (__bf16)(r0 * cs - r1 * sn);
-            dst[kDc + 2 * t + 1] = (__bf16)(r0 * sn + r1 * cs);
-        }
+    red[t >> 6][t & 63] = acc;
+    __syncthreads();
+    if (t >= 64) return;
+    const float val = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    __bf16* dst = cache + ((size_t)m * t_max + pos) * kDqk + cb * 64;
+    if (cb < NCB - 1) {
+        dst[t] = (__bf16)val;
+    } else {
+        // RoPE block: lanes 2j and 2j+1 (of the one wave left) hold the pair
+        const float other = __shfl_xor(val, 1, 64);
+        const int j = t >> 1;
+        const float r0 = (t & 1) ? other : val, r1 = (t & 1) ? val : other;
+        const float cs = rope_cos[(size_t)pos * (kDr / 2) + j];
+        const float sn = rope_sin[(size_t)pos * (kDr / 2) + j];
+        dst[t] = (__bf16)((t & 1) ? r0 * sn + r1 * cs : r0 * cs - r1 * sn);
     }
-    if (seqlens_out != nullptr && t == 0) seqlens_out[m] = write ? pos + 1 : pos;
 }
 
 constexpr int kAbsorbQSlabs = 4;  // 64-column weight slabs per q-absorb workgroup
@@ -370,9 +390,15 @@ hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const vo
     return hipGetLastError();
 }
 
+// Workspace: fp32 partial sums [b][H][576], then a copy of the b positions.
+size_t append_part_bytes(int b, int d_model)
+{
+    return align_up((size_t)b * (size_t)(d_model / kAppendKD) * kDqk * sizeof(float), 256);
+}
+
 size_t append_workspace_bytes(int b, int d_model)
 {
-    return (size_t)b * (size_t)(d_model / kAppendKD) * kDqk * sizeof(float);
+    return append_part_bytes(b, d_model) + align_up((size_t)b * sizeof(int32_t), 256);
 }
 
 int append_kd() { return kAppendKD; }
@@ -380,15 +406,17 @@ int append_kd() { return kAppendKD; }
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
                                const void* w_dkv, const void* w_kr, const float* rope_cos,
                                const float* rope_sin, void* cache, const int32_t* seqlens,
-                               int32_t* seqlens_out, float* part, hipStream_t stream)
+                               int32_t* seqlens_out, void* workspace, hipStream_t stream)
 {
     const int H = d_model / kAppendKD;
+    float* part = (float*)workspace;
+    int32_t* wpos = (int32_t*)((unsigned char*)workspace + append_part_bytes(b, d_model));
     append_proj_kernel<<<H * (kDc / 64 + 1), 256, 0, stream>>>(b, H, (const __bf16*)x, (const __bf16*)w_dkv,
-                                                               (const __bf16*)w_kr, part);
+                                                               (const __bf16*)w_kr, part, seqlens, wpos);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    append_finish_kernel<<<b, 256, 0, stream>>>(H, t_max, n_pos, part, rope_cos, rope_sin, (__bf16*)cache,
-                                                seqlens, seqlens_out);
+    append_finish_kernel<<<b * (kDqk / 64), 256, 0, stream>>>(H, t_max, n_pos, part, wpos, rope_cos, rope_sin,
+                                                              (__bf16*)cache, seqlens_out);
     return hipGetLastError();
 }
 

@@ -572,7 +572,7 @@ mla_status_t mla_absorb_q(mla_dtype_t dt, int b, int h, const void* q_nope, cons
 size_t mla_cache_append_workspace_bytes(int b, int d_model)
 {
     if (b <= 0 || d_model <= 0 || d_model % append_kd() != 0) return 0;
-    return align_up(append_workspace_bytes(b, d_model), 256);
+    return append_workspace_bytes(b, d_model);
 }
 
 mla_status_t mla_cache_append(mla_dtype_t dt, int b, int d_model, int t_max, const void* x,
@@ -596,8 +596,7 @@ mla_status_t mla_cache_append(mla_dtype_t dt, int b, int d_model, int t_max, con
         return MLA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < mla_cache_append_workspace_bytes(b, d_model)) return MLA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(launch_cache_append(b, d_model, t_max, n_pos, x, w_dkv, w_kr, rope_cos, rope_sin,
-                                          cache, seqlens, seqlens_out, (float*)workspace,
-                                          (hipStream_t)stream));
+                                          cache, seqlens, seqlens_out, workspace, (hipStream_t)stream));
 }
 
 mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,

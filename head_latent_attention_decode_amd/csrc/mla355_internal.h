@@ -138,12 +138,13 @@ hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w
                            hipStream_t stream);
 
 // Appending a token's latent row: the hidden dimension must be a multiple of
-// append_kd(); the partial sums take append_workspace_bytes(b, d_model).
+// append_kd(); the workspace (partial sums and a copy of the positions) takes
+// append_workspace_bytes(b, d_model).
 int append_kd();
 size_t append_workspace_bytes(int b, int d_model);
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
                                const void* w_dkv, const void* w_kr, const float* rope_cos,
                                const float* rope_sin, void* cache, const int32_t* seqlens,
-                               int32_t* seqlens_out, float* part, hipStream_t stream);
+                               int32_t* seqlens_out, void* workspace, hipStream_t stream);
 
 }  // namespace mla355

@@ -217,7 +217,7 @@ const char* mla_decode_mtp_kernel_name(mla_dtype_t dtype, int q_len, int h);
  * Layouts: x [b, d_model] bf16; w_dkv [d_model, 512] bf16; w_kr [d_model, 64]
  * bf16 (row-major); cache [b, t_max, 576] bf16 (updated in place).
  * workspace: device scratch of at least mla_cache_append_workspace_bytes(b,
- * d_model) bytes (fp32 partial sums), 256-byte aligned.
+ * d_model) bytes (fp32 partial sums and a copy of seqlens), 256-byte aligned.
  * Errors (host side, before any launch): MLA_ERR_UNSUPPORTED for dtype
  * MLA_DTYPE_F32; MLA_ERR_INVALID_ARGUMENT for an unknown dtype, a null pointer
  * (seqlens_out excepted), x / w_dkv / w_kr / cache not 16-byte aligned, the

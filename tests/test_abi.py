@@ -283,10 +283,12 @@ def test_cache_append_validation(mla, kw, status):
 
 
 def test_cache_append_workspace(mla):
-    # fp32 partial sums: one 576-wide row per batch row and 256-wide hidden chunk
-    assert mla.mla_cache_append_workspace_bytes(64, 7168) == 64 * 28 * 576 * 4
-    assert mla.mla_cache_append_workspace_bytes(3, 256) == 3 * 576 * 4  # a multiple of 256 already
-    assert mla.mla_cache_append_workspace_bytes(1, 256) == 2304
-    assert mla.mla_cache_append_workspace_bytes(5, 256) == -(-5 * 576 * 4 // 256) * 256
+    # fp32 partial sums (one 576-wide row per batch row and 256-wide hidden
+    # chunk) and a copy of the b positions, each rounded up to 256 bytes
+    up = lambda n: -(-n // 256) * 256
+    assert mla.mla_cache_append_workspace_bytes(64, 7168) == 64 * 28 * 576 * 4 + 256
+    assert mla.mla_cache_append_workspace_bytes(3, 256) == 3 * 576 * 4 + 256
+    assert mla.mla_cache_append_workspace_bytes(5, 256) == up(5 * 576 * 4) + 256
+    assert mla.mla_cache_append_workspace_bytes(100, 512) == up(100 * 2 * 576 * 4) + up(400)
     assert mla.mla_cache_append_workspace_bytes(64, 7000) == 0
     assert mla.mla_cache_append_workspace_bytes(0, 7168) == 0
