@@ -102,6 +102,14 @@ _lib.mla_cache_append_workspace_bytes.argtypes = [_ci, _ci]
 _lib.mla_cache_append.restype = _ci
 _lib.mla_cache_append.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _vp, _vp, _ci, _vp, _vp, _vp, _vp,
                                   _sz, _vp]
+_lib.mla_cache_append_paged.restype = _ci
+_lib.mla_cache_append_paged.argtypes = [_ci, _ci, _ci, _vp, _vp, _vp, _vp, _vp, _ci, _vp, _ci, _ci, _vp, _ci,
+                                        _vp, _vp, _vp, _sz, _vp]
+_lib.mla_decode_mtp_paged_workspace_bytes.restype = _sz
+_lib.mla_decode_mtp_paged_workspace_bytes.argtypes = [_ci, _ci, _ci, _ci, _ci, _ci, _ci]
+_lib.mla_decode_mtp_paged.restype = _ci
+_lib.mla_decode_mtp_paged.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _ci, _ci, _vp, _ci, _vp, _cf, _vp, _vp,
+                                      _vp, _sz, _vp]
 
 EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla_absorb_o",
                     "mla_decode_workspace_bytes", "mla_decode_workspace_bytes_ex", "mla_decode",
@@ -111,7 +119,8 @@ EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla
                     "mla_decode_fp8_ex", "mla_decode_fp8_kernel_name",
                     "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name",
                     "mla_decode_mtp_workspace_bytes_ex", "mla_decode_mtp_ex",
-                    "mla_cache_append_workspace_bytes", "mla_cache_append")
+                    "mla_cache_append_workspace_bytes", "mla_cache_append", "mla_cache_append_paged",
+                    "mla_decode_mtp_paged_workspace_bytes", "mla_decode_mtp_paged")
 
 
 class MLAError(RuntimeError):
@@ -338,6 +347,70 @@ def mla_cache_append(x, w_dkv, w_kr, rope_cos, rope_sin, cache, seqlens, seqlens
                                _stream(stream))
     _check(st, "mla_cache_append")
     return cache
+
+
+def mla_cache_append_paged(x, w_dkv, w_kr, rope_cos, rope_sin, kv_pool, block_table, seqlens,
+                           seqlens_out=None, workspace=None, stream=None):
+    """mla_cache_append into a paged pool [num_blocks, block_size, 576] through
+    block_table [b, max_blocks] int32.  Returns kv_pool."""
+    b, d_model = x.shape
+    nb, bs = kv_pool.shape[0], kv_pool.shape[1]
+    mb = block_table.shape[1]
+    n_pos = rope_cos.shape[0]
+    dev = x.device
+    need = mla_cache_append_workspace_bytes(b, d_model)
+    if need == 0:
+        raise ValueError("invalid append problem: b=%d d_model=%d" % (b, d_model))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    so = None if seqlens_out is None else _dev(seqlens_out, "seqlens_out", (b,), torch.int32)
+    st = _lib.mla_cache_append_paged(MLA_DTYPE_BF16, b, d_model,
+                                     _dev(x, "x", (b, d_model), torch.bfloat16),
+                                     _dev(w_dkv, "w_dkv", (d_model, D_C), torch.bfloat16),
+                                     _dev(w_kr, "w_kr", (d_model, D_R), torch.bfloat16),
+                                     _dev(rope_cos, "rope_cos", (n_pos, D_R // 2), torch.float32),
+                                     _dev(rope_sin, "rope_sin", (n_pos, D_R // 2), torch.float32), n_pos,
+                                     _dev(kv_pool, "kv_pool", (nb, bs, D_QK), torch.bfloat16), nb, bs,
+                                     _dev(block_table, "block_table", (b, mb), torch.int32), mb,
+                                     _dev(seqlens, "seqlens", (b,), torch.int32), so,
+                                     ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                                     _stream(stream))
+    _check(st, "mla_cache_append_paged")
+    return kv_pool
+
+
+def mla_decode_mtp_paged(q_prime, kv_pool, block_table, seqlens, softmax_scale, out=None, lse=None,
+                         workspace=None, stream=None):
+    """mla_decode_mtp over a paged pool.  q_prime [b,q_len,h,576] bf16, kv_pool
+    [num_blocks,block_size,576], block_table [b,max_blocks] int32."""
+    b, q_len, h, _ = q_prime.shape
+    nb, bs = kv_pool.shape[0], kv_pool.shape[1]
+    mb = block_table.shape[1]
+    dt = q_prime.dtype
+    dev = q_prime.device
+    if dt != torch.bfloat16:
+        raise TypeError("mla_decode_mtp_paged takes bf16 tensors")
+    if out is None:
+        out = torch.empty((b, q_len, h, D_C), dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((b, q_len, h), dtype=torch.float32, device=dev)
+    need = int(_lib.mla_decode_mtp_paged_workspace_bytes(MLA_DTYPE_BF16, b, q_len, h, nb, bs, mb))
+    if need == 0:
+        raise ValueError("invalid paged problem: b=%d q_len=%d h=%d block_size=%d" % (b, q_len, h, bs))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.mla_decode_mtp_paged(MLA_DTYPE_BF16, b, q_len, h,
+                                   _dev(q_prime, "q_prime", (b, q_len, h, D_QK), dt),
+                                   _dev(kv_pool, "kv_pool", (nb, bs, D_QK), dt), nb, bs,
+                                   _dev(block_table, "block_table", (b, mb), torch.int32), mb,
+                                   _dev(seqlens, "seqlens", (b,), torch.int32),
+                                   ctypes.c_float(float(softmax_scale)),
+                                   _dev(out, "out", (b, q_len, h, D_C), dt),
+                                   _dev(lse, "lse", (b, q_len, h), torch.float32),
+                                   ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                                   _stream(stream))
+    _check(st, "mla_decode_mtp_paged")
+    return out, lse
 
 
 def mla_decode_paged_kernel_name(h: int, config=None):

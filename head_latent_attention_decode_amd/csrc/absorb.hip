@@ -324,20 +324,33 @@ __global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __
 // race with the other blocks' reads); nothing is written when pos is outside
 // [0, min(t_max, n_pos)).  Block 0 writes seqlens_out[m] (may be null or equal
 // to seqlens): pos + 1 for a written row, pos otherwise.
+//
+// Paged pool (block_table != null): cache is the pool [num_blocks,
+// block_size, 576]; row pos of batch row m is row pos % block_size of block
+// block_table[m * max_blocks + pos / block_size] (t_max = max_blocks *
+// block_size); an entry outside [0, num_blocks) means no write.
 __global__ __launch_bounds__(256) void append_finish_kernel(int H, int t_max, int n_pos,
                                                             const float* __restrict__ part,
                                                             const int32_t* __restrict__ wpos,
                                                             const float* __restrict__ rope_cos,
                                                             const float* __restrict__ rope_sin,
                                                             __bf16* __restrict__ cache,
-                                                            int32_t* seqlens_out)
+                                                            int32_t* seqlens_out,
+                                                            const int32_t* __restrict__ block_table,
+                                                            int num_blocks, int block_size, int max_blocks)
 {
     __shared__ float red[4][64];
     constexpr int NCB = kDqk / 64;
     const int m = blockIdx.x / NCB, cb = blockIdx.x % NCB;
     const int t = threadIdx.x;
     const int pos = wpos[m];
-    const bool write = pos >= 0 && pos < t_max && pos < n_pos;
+    bool write = pos >= 0 && pos < t_max && pos < n_pos;
+    size_t row_off = (size_t)m * t_max + pos;  // destination row (contiguous cache)
+    if (write && block_table != nullptr) {
+        const int blk = block_table[(size_t)m * max_blocks + pos / block_size];
+        write = blk >= 0 && blk < num_blocks;
+        row_off = (size_t)blk * block_size + pos % block_size;
+    }
     if (cb == 0 && t == 0 && seqlens_out != nullptr) seqlens_out[m] = write ? pos + 1 : pos;
     if (!write) return;
     const int col = cb * 64 + (t & 63);
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(256) void append_finish_kernel(int H, int t_max, in
     __syncthreads();
     if (t >= 64) return;
     const float val = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
-    __bf16* dst = cache + ((size_t)m * t_max + pos) * kDqk + cb * 64;
+    __bf16* dst = cache + row_off * kDqk + cb * 64;
     if (cb < NCB - 1) {
         dst[t] = (__bf16)val;
     } else {
@@ -406,7 +419,9 @@ int append_kd() { return kAppendKD; }
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
                                const void* w_dkv, const void* w_kr, const float* rope_cos,
                                const float* rope_sin, void* cache, const int32_t* seqlens,
-                               int32_t* seqlens_out, void* workspace, hipStream_t stream)
+                               int32_t* seqlens_out, void* workspace, hipStream_t stream,
+                               const int32_t* block_table, int num_blocks, int block_size,
+                               int max_blocks)
 {
     const int H = d_model / kAppendKD;
     float* part = (float*)workspace;
@@ -416,7 +431,8 @@ hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const v
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     append_finish_kernel<<<b * (kDqk / 64), 256, 0, stream>>>(H, t_max, n_pos, part, wpos, rope_cos, rope_sin,
-                                                              (__bf16*)cache, seqlens_out);
+                                                              (__bf16*)cache, seqlens_out, block_table,
+                                                              num_blocks, block_size, max_blocks);
     return hipGetLastError();
 }
 

@@ -596,7 +596,109 @@ mla_status_t mla_cache_append(mla_dtype_t dt, int b, int d_model, int t_max, con
         return MLA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < mla_cache_append_workspace_bytes(b, d_model)) return MLA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(launch_cache_append(b, d_model, t_max, n_pos, x, w_dkv, w_kr, rope_cos, rope_sin,
-                                          cache, seqlens, seqlens_out, workspace, (hipStream_t)stream));
+                                          cache, seqlens, seqlens_out, workspace, (hipStream_t)stream,
+                                          nullptr, 0, 0, 0));
+}
+
+mla_status_t mla_cache_append_paged(mla_dtype_t dt, int b, int d_model, const void* x,
+                                    const void* w_dkv, const void* w_kr, const float* rope_cos,
+                                    const float* rope_sin, int n_pos, void* kv_pool, int num_blocks,
+                                    int block_size, const int32_t* block_table, int max_blocks,
+                                    const int32_t* seqlens, int32_t* seqlens_out, void* workspace,
+                                    size_t workspace_bytes, void* stream)
+{
+    if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
+    if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+    if (d_model <= 0 || d_model % append_kd() != 0 || n_pos <= 0) return MLA_ERR_INVALID_ARGUMENT;
+    if (!paged_dims_ok(b, 1, num_blocks, block_size, max_blocks)) return MLA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)b * d_model >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!x || !w_dkv || !w_kr || !rope_cos || !rope_sin || !kv_pool || !block_table || !seqlens ||
+        !workspace)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(kv_pool) ||
+        ((uintptr_t)rope_cos & 3u) != 0 || ((uintptr_t)rope_sin & 3u) != 0 ||
+        ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seqlens & 3u) != 0 ||
+        ((uintptr_t)seqlens_out & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < mla_cache_append_workspace_bytes(b, d_model)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_cache_append(b, d_model, max_blocks * block_size, n_pos, x, w_dkv, w_kr,
+                                          rope_cos, rope_sin, kv_pool, seqlens, seqlens_out, workspace,
+                                          (hipStream_t)stream, block_table, num_blocks, block_size,
+                                          max_blocks));
+}
+
+size_t mla_decode_mtp_paged_workspace_bytes(mla_dtype_t dt, int b, int q_len, int h, int num_blocks,
+                                            int block_size, int max_blocks)
+{
+    if (dt != MLA_DTYPE_BF16 || q_len <= 0 || h <= 0 || (int64_t)q_len * h > ((int64_t)1 << 20)) return 0;
+    if (!paged_dims_ok(b, q_len * h, num_blocks, block_size, max_blocks)) return 0;
+    if (q_len == 1) return mla_decode_paged_workspace_bytes(dt, b, h, num_blocks, block_size, max_blocks, nullptr);
+    const MtpSchedule s = choose_mtp_schedule(q_len * h);
+    return workspace_layout(b, q_len * h, s.n_chunks, 2).total;
+}
+
+mla_status_t mla_decode_mtp_paged(mla_dtype_t dt, int b, int q_len, int h, const void* q_prime,
+                                  const void* kv_pool, int num_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream)
+{
+    if (!dtype_ok(dt)) return MLA_ERR_INVALID_ARGUMENT;
+    if (dt != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+    if (q_len <= 0 || h <= 0 || (int64_t)q_len * h > ((int64_t)1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+    if (q_len == 1)
+        return mla_decode_paged_ex(dt, b, h, q_prime, kv_pool, num_blocks, block_size, block_table,
+                                   max_blocks, seqlens, softmax_scale, out, lse, workspace,
+                                   workspace_bytes, nullptr, stream);
+    const int rows = q_len * h;
+    if (!paged_dims_ok(b, rows, num_blocks, block_size, max_blocks)) return MLA_ERR_INVALID_ARGUMENT;
+    if (!q_prime || !kv_pool || !block_table || !seqlens || !out || !lse || !workspace)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_prime) || !aligned16(kv_pool) || !aligned16(block_table) ||
+        !aligned16(seqlens) || !aligned16(out) || !aligned16(lse) ||
+        ((uintptr_t)workspace & 255u) != 0)
+        return MLA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+    const MtpSchedule s = choose_mtp_schedule(rows);
+    const WorkspaceLayout w = workspace_layout(b, rows, s.n_chunks, 2);
+    if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    const int t_max = max_blocks * block_size;
+
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    int32_t* plan = (int32_t*)ws;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = kv_pool;
+    p.plan = plan;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (void*)(ws + w.po_off);
+    p.block_table = block_table;
+    p.cache_scale = nullptr;
+    p.seqlens = seqlens;
+    p.num_blocks = num_blocks;
+    p.block_size = block_size;
+    p.max_blocks = max_blocks;
+    p.q_len = q_len;
+    p.heads_per_token = h;
+    p.b = b;
+    p.h = rows;
+    p.t_max = t_max;
+    p.n_chunks = s.n_chunks;
+    p.n_hg = s.n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    // tile-aligned plan: every segment starts at a multiple of 32 tokens
+    hipError_t e = launch_plan(seqlens, b, rows, t_max, s.n_chunks, 32, 32, plan, true, out, lse, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    e = s.nw == 4   ? launch_decode_wide_causal<4, 2>(p, hs)
+        : s.nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
+                    : launch_decode_wide_causal<1, 3>(p, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    e = launch_combine(true, plan, b, rows, p.plse, p.po, out, lse, hs);
+    return hip_status(e);
 }
 
 mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,

@@ -142,9 +142,13 @@ hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w
 // append_workspace_bytes(b, d_model).
 int append_kd();
 size_t append_workspace_bytes(int b, int d_model);
+// block_table == nullptr: cache [b, t_max, 576]; else cache is the pool
+// [num_blocks, block_size, 576] and t_max = max_blocks * block_size.
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
                                const void* w_dkv, const void* w_kr, const float* rope_cos,
                                const float* rope_sin, void* cache, const int32_t* seqlens,
-                               int32_t* seqlens_out, void* workspace, hipStream_t stream);
+                               int32_t* seqlens_out, void* workspace, hipStream_t stream,
+                               const int32_t* block_table, int num_blocks, int block_size,
+                               int max_blocks);
 
 }  // namespace mla355

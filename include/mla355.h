@@ -233,6 +233,41 @@ mla_status_t mla_cache_append(mla_dtype_t dtype, int b, int d_model, int t_max, 
                               void* stream);
 
 /*
+ * mla_cache_append_paged -- mla_cache_append into a paged latent cache (the
+ * pool and block table of mla_decode_paged).  Batch row i's new row pos =
+ * seqlens[i] goes to row pos % block_size of block
+ * block_table[i * max_blocks + pos / block_size]; nothing is written when pos
+ * is outside [0, min(max_blocks * block_size, n_pos)) or that table entry is
+ * outside [0, num_blocks) (a write is never redirected into another block).
+ * seqlens_out as in mla_cache_append (pos + 1 only for a written row).
+ * kv_pool [num_blocks, block_size, 576] bf16 (updated in place); block_table
+ * [b, max_blocks] int32; other arguments as in mla_cache_append.
+ * Errors: those of mla_cache_append, with the pool checks of mla_decode_paged
+ * (block_size a positive multiple of 32, num_blocks > 0, max_blocks > 0, the
+ * table 4-byte aligned) in place of the t_max checks.
+ */
+mla_status_t mla_cache_append_paged(mla_dtype_t dtype, int b, int d_model, const void* x,
+                                    const void* w_dkv, const void* w_kr, const float* rope_cos,
+                                    const float* rope_sin, int n_pos, void* kv_pool, int num_blocks,
+                                    int block_size, const int32_t* block_table, int max_blocks,
+                                    const int32_t* seqlens, int32_t* seqlens_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_mtp_paged -- mla_decode_mtp over a paged latent cache (pool and
+ * block table as in mla_decode_paged; the q_len new tokens are the last q_len
+ * rows of each sequence).  q_len = 1 is exactly mla_decode_paged.
+ * Errors: those of mla_decode_mtp with the pool checks of mla_decode_paged.
+ */
+size_t mla_decode_mtp_paged_workspace_bytes(mla_dtype_t dtype, int b, int q_len, int h,
+                                            int num_blocks, int block_size, int max_blocks);
+mla_status_t mla_decode_mtp_paged(mla_dtype_t dtype, int b, int q_len, int h, const void* q_prime,
+                                  const void* kv_pool, int num_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode_paged -- mla_decode over a paged latent cache.  The cached rows
  * of every sequence live in fixed-size blocks of a shared pool, found through
  * a block table (glossary, capacity and cost section: MLA leaves dynamic

@@ -292,3 +292,54 @@ def test_cache_append_workspace(mla):
     assert mla.mla_cache_append_workspace_bytes(100, 512) == up(100 * 2 * 576 * 4) + up(400)
     assert mla.mla_cache_append_workspace_bytes(64, 7000) == 0
     assert mla.mla_cache_append_workspace_bytes(0, 7168) == 0
+
+
+def _append_paged(lib, dt=1, b=4, dm=512, x=A, wd=A, wr=A, cs=A, sn=A, npos=64, pool=A, nb=8, bs=64,
+                  bt=A, mb=4, sl=A, so=0, ws=A, wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_cache_append_paged(dt, b, dm, vp(x), vp(wd), vp(wr), vp(cs), vp(sn), npos, vp(pool), nb,
+                                      bs, vp(bt), mb, vp(sl), vp(so), vp(ws), ctypes.c_size_t(wsb), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dt": 0}, 2), ({"dt": 3}, 1), ({"b": 0}, 1), ({"dm": 300}, 1), ({"npos": 0}, 1), ({"nb": 0}, 1),
+    ({"bs": 48}, 1), ({"bs": 0}, 1), ({"mb": 0}, 1), ({"pool": 0}, 1), ({"bt": 0}, 1), ({"sl": 0}, 1),
+    ({"x": 0}, 1), ({"pool": A + 8}, 1), ({"bt": A + 2}, 1), ({"so": A + 2}, 1), ({"ws": A + 64}, 1),
+    ({"wsb": 100}, 3),
+])
+def test_cache_append_paged_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _append_paged(lib, **kw) == status
+
+
+def _mtp_paged(lib, dt=1, b=2, ql=2, h=16, q=A, pool=A, nb=8, bs=64, bt=A, mb=4, sl=A, scale=SCALE,
+               out=A, lse=A, ws=A, wsb=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.mla_decode_mtp_paged(dt, b, ql, h, vp(q), vp(pool), nb, bs, vp(bt), mb, vp(sl),
+                                    ctypes.c_float(scale), vp(out), vp(lse), vp(ws), ctypes.c_size_t(wsb),
+                                    vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dt": 0}, 2), ({"dt": 7}, 1), ({"ql": 0}, 1), ({"h": 0}, 1), ({"bs": 40}, 1), ({"nb": 0}, 1),
+    ({"mb": 0}, 1), ({"q": 0}, 1), ({"pool": 0}, 1), ({"bt": 0}, 1), ({"sl": 0}, 1), ({"out": 0}, 1),
+    ({"lse": 0}, 1), ({"ws": 0}, 1), ({"q": A + 8}, 1), ({"ws": A + 16}, 1), ({"scale": 0.0}, 1),
+    ({"wsb": 1024}, 3),
+    # one query token: the same validation as mla_decode_paged
+    ({"ql": 1, "bs": 40}, 1), ({"ql": 1, "pool": 0}, 1), ({"ql": 1, "wsb": 1024}, 3),
+])
+def test_decode_mtp_paged_validation(mla, kw, status):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert _mtp_paged(lib, **kw) == status
+
+
+def test_decode_mtp_paged_workspace(mla):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    lib.mla_decode_mtp_paged_workspace_bytes.restype = ctypes.c_size_t
+    # the same workspace as the contiguous multi-token call of the same rows
+    assert lib.mla_decode_mtp_paged_workspace_bytes(1, 64, 2, 128, 4096, 64, 64) == \
+        mla.mla_decode_mtp_workspace_bytes(64, 2, 128, 4096)
+    assert lib.mla_decode_mtp_paged_workspace_bytes(1, 64, 1, 128, 4096, 64, 64) == \
+        mla.mla_decode_paged_workspace_bytes(64, 128, 4096, 64, 64)
+    assert lib.mla_decode_mtp_paged_workspace_bytes(1, 64, 2, 128, 4096, 48, 64) == 0
+    assert lib.mla_decode_mtp_paged_workspace_bytes(0, 64, 2, 128, 4096, 64, 64) == 0

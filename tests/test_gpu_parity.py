@@ -593,3 +593,61 @@ def test_cache_append_dsv3_b64(mla):
     got = np.stack([to_np(cache[r, 4095]) for r in rows])
     assert_out(got, ref[:, 4095], BF16_OUT_REL, "appended rows")
     assert torch.equal(cache[:, :4095], before[:, :4095])
+
+
+# ---- paged forms of the multi-token decode and the append ---------------------
+
+@pytest.mark.parametrize("q_len,h,lens,bs", [
+    (2, 128, [700, 257, 1000, 33, 2], 64), (3, 16, [100, 3, 1, 0, 64], 32), (4, 32, [129, 4, 96], 128),
+], ids=["q2-h128-bs64", "q3-h16-bs32", "q4-h32-bs128"])
+def test_mtp_paged_every_output(mla, q_len, h, lens, bs):
+    b = len(lens)
+    w, q = _mtp_workload(b, q_len, h, lens, seed=710 + q_len * h + bs)
+    pool, bt = _paginate(w, bs, seed=q_len + bs, unused_entry=-777)
+    out, lse = mla.mla_decode_mtp_paged(q, pool, bt, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode_latent_causal(q.cpu(), w.cache.cpu(), w.seqlens.cpu().numpy(), w.scale)
+    assert_out(to_np(out), ref_o, BF16_OUT_REL)
+    assert_lse(to_np(lse), ref_l, BF16_LSE_ABS)
+    # the contiguous call agrees within the same tolerance
+    out_c, lse_c = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
+    assert_out(to_np(out), to_np(out_c), BF16_OUT_REL)
+
+
+def test_cache_append_paged(mla):
+    # rows scattered over a shuffled pool; the written block comes from the table
+    lens = [0, 70, 127, 128, 200, 63]
+    b, bs, mb, d_model = len(lens), 64, 4, 512
+    nb = b * mb + 2
+    x, wd, wr, cos_t, sin_t, _ = _append_inputs(b, d_model, 1, bs * mb, seed=99)
+    g = torch.Generator().manual_seed(100)
+    pool = torch.randn(nb, bs, 576, generator=g).to(torch.bfloat16).cuda()
+    bt = torch.randperm(nb, generator=g)[: b * mb].reshape(b, mb).to(torch.int32)
+    bt[5, 0] = nb + 3   # row 5 writes at position 63 of block 0: out of the pool, no write
+    bt = bt.cuda()
+    before = pool.clone()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sl_out = torch.empty_like(sl)
+    mla.mla_cache_append_paged(x, wd, wr, cos_t, sin_t, pool, bt, sl, sl_out)
+    torch.cuda.synchronize()
+    assert sl_out.cpu().tolist() == [1, 71, 128, 129, 201, 63]
+    # the oracle appends into the gathered contiguous view; compare the written rows
+    btc = bt.long().cpu()
+    gathered = torch.zeros(b, mb * bs, 576, dtype=torch.bfloat16)
+    for i in range(b):
+        for k in range(mb):
+            if 0 <= btc[i, k] < nb:
+                gathered[i, k * bs:(k + 1) * bs] = before[btc[i, k]].cpu()
+    ref = oracle.cache_append(x.cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(), np.array(lens, np.int32),
+                              gathered)
+    changed = torch.zeros(nb, bs, dtype=torch.bool)
+    got, want = [], []
+    for i, L in enumerate(lens):
+        if i == 5:
+            continue
+        blk, r = int(btc[i, L // bs]), L % bs
+        changed[blk, r] = True
+        got.append(to_np(pool[blk, r]))
+        want.append(ref[i, L])
+    assert_out(np.stack(got), np.stack(want), BF16_OUT_REL, "appended rows")
+    assert torch.equal(pool.cpu()[~changed], before.cpu()[~changed]), "other pool rows changed"
