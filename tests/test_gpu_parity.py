@@ -651,3 +651,21 @@ def test_cache_append_paged(mla):
         want.append(ref[i, L])
     assert_out(np.stack(got), np.stack(want), BF16_OUT_REL, "appended rows")
     assert torch.equal(pool.cpu()[~changed], before.cpu()[~changed]), "other pool rows changed"
+
+
+@pytest.mark.parametrize("h", [16, 128])
+def test_large_batch_short_rows(mla, h):
+    # more batch rows than the plan kernel's grid (its workgroups then loop over
+    # rows): many short and empty rows; sampled rows against the oracle, every
+    # empty row exactly zero
+    b = 3000
+    g = torch.Generator().manual_seed(120 + h)
+    lens = torch.randint(0, 101, (b,), generator=g)
+    lens[::7] = 0
+    w = workloads.make_custom(b, h, lens.tolist(), seed=121 + h, device="cuda")
+    out, lse = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2, 1499, 2047, 2048, 2049, 2998, 2999] + list(range(3, 3000, 97))
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, rows)
+    empty = (lens == 0).nonzero().flatten().tolist()
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
