@@ -147,8 +147,60 @@ bool dtype_ok(mla_dtype_t dt) { return dt == MLA_DTYPE_F32 || dt == MLA_DTYPE_BF
 
 mla_status_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Launch parameters shared by every split-KV attention call: inputs, outputs
+// and the workspace carved by `w` (plan first, then the partial lse and the
+// partial outputs), for `rows` query rows per batch row.  The cache form (a
+// paged pool, fp8 scales, causal query tokens) is set by the caller.
+DecodeParams split_params(const void* q_prime, const void* cache, const int32_t* seqlens, void* out,
+                          float* lse, void* workspace, const WorkspaceLayout& w, int b, int rows,
+                          int t_max, int n_chunks, int n_hg, float softmax_scale)
+{
+    unsigned char* ws = (unsigned char*)workspace;
+    DecodeParams p;
+    p.q = q_prime;
+    p.cache = cache;
+    p.plan = (const int32_t*)ws;
+    p.out = out;
+    p.lse = lse;
+    p.plse = (float*)(ws + w.plse_off);
+    p.po = (void*)(ws + w.po_off);
+    p.block_table = nullptr;
+    p.seqlens = seqlens;
+    p.cache_scale = nullptr;
+    p.num_blocks = p.block_size = p.max_blocks = 0;
+    p.q_len = 1;
+    p.heads_per_token = rows;
+    p.b = b;
+    p.h = rows;
+    p.t_max = t_max;
+    p.n_chunks = n_chunks;
+    p.n_hg = n_hg;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return p;
+}
+
+// plan -> attention kernel -> combine on `hs`, with the caller's profiling
+// events (if any) recorded right before and after the attention kernel.
+// align > 1 lays the plan over lengths rounded up to whole tiles (paged pool).
+template <typename Kernel>
+mla_status_t run_split(const DecodeParams& p, bool bf16, int min_chunk, int align,
+                       const mla_decode_config_t* cfg, hipStream_t hs, Kernel&& kernel)
+{
+    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
+    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
+    hipError_t e = launch_plan(p.seqlens, p.b, p.h, p.t_max, p.n_chunks, min_chunk, align,
+                               const_cast<int32_t*>(p.plan), bf16, p.out, p.lse, hs);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
+    if (kernel() != hipSuccess) return MLA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
+    return hip_status(launch_combine(bf16, p.plan, p.b, p.h, p.plse, p.po, p.out, p.lse, hs));
+}
+
 }  // namespace
 
+// Everything is built with hidden visibility; only the C ABI is exported.
+#pragma GCC visibility push(default)
 extern "C" {
 
 int mla_abi_version(void) { return MLA355_ABI_VERSION; }
@@ -205,44 +257,13 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks, dt == MLA_DTYPE_BF16 ? 2 : 4);
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
-    hipStream_t hs = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    int32_t* plan = (int32_t*)ws;
-    DecodeParams p;
-    p.q = q_prime;
-    p.cache = cache;
-    p.plan = plan;
-    p.out = out;
-    p.lse = lse;
-    p.plse = (float*)(ws + w.plse_off);
-    p.po = (void*)(ws + w.po_off);
-    p.block_table = nullptr;
-    p.cache_scale = nullptr;
-    p.seqlens = seqlens;
-    p.num_blocks = p.block_size = p.max_blocks = 0;
-    p.q_len = 1;
-    p.heads_per_token = h;
-    p.b = b;
-    p.h = h;
-    p.t_max = t_max;
-    p.n_chunks = s.n_chunks;
-    p.n_hg = s.n_hg;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
-    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
-    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, 1, plan,
-                               dt == MLA_DTYPE_BF16, out, lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
-    if (dt == MLA_DTYPE_BF16)
-        e = launch_decode_bf16(p, s.hpg, s.variant, hs);
-    else
-        e = launch_decode_f32(p, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_combine(dt == MLA_DTYPE_BF16, plan, b, h, p.plse, p.po, out, lse, hs);
-    return hip_status(e);
+    const bool bf16 = dt == MLA_DTYPE_BF16;
+    DecodeParams p = split_params(q_prime, cache, seqlens, out, lse, workspace, w, b, h, t_max,
+                                  s.n_chunks, s.n_hg, softmax_scale);
+    return run_split(p, bf16, s.min_chunk, 1, cfg, (hipStream_t)stream, [&] {
+        return bf16 ? launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream)
+                    : launch_decode_f32(p, (hipStream_t)stream);
+    });
 }
 
 mla_status_t mla_decode(mla_dtype_t dt, int b, int h, int t_max, const void* q_prime,
@@ -253,14 +274,22 @@ mla_status_t mla_decode(mla_dtype_t dt, int b, int h, int t_max, const void* q_p
                          workspace, workspace_bytes, nullptr, stream);
 }
 
-bool mtp_dims_ok(int b, int q_len, int h, int t_max)
+static bool mtp_dims_ok(int b, int q_len, int h, int t_max)
 {
     if (q_len <= 0 || h <= 0 || (int64_t)q_len * h > ((int64_t)1 << 20)) return false;
     return dims_ok(b, q_len * h, t_max);
 }
 
+// The causal kernel for `nw` waves of 32 query rows.
+static hipError_t launch_mtp(const DecodeParams& p, int nw, hipStream_t hs)
+{
+    return nw == 4 ? launch_decode_wide_causal<4, 2>(p, hs)
+           : nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
+                     : launch_decode_wide_causal<1, 3>(p, hs);
+}
+
 // Config of the multi-token call: only n_chunks and the profiling events may be set.
-mla_status_t check_mtp_config(const mla_decode_config_t* cfg)
+static mla_status_t check_mtp_config(const mla_decode_config_t* cfg)
 {
     if (!cfg) return MLA_OK;
     for (int i = 0; i < 5; ++i)
@@ -272,7 +301,7 @@ mla_status_t check_mtp_config(const mla_decode_config_t* cfg)
     return MLA_OK;
 }
 
-MtpSchedule mtp_schedule(int rows, const mla_decode_config_t* cfg)
+static MtpSchedule mtp_schedule(int rows, const mla_decode_config_t* cfg)
 {
     MtpSchedule s = choose_mtp_schedule(rows);
     if (cfg && cfg->n_chunks != 0) s.n_chunks = cfg->n_chunks;
@@ -329,42 +358,11 @@ mla_status_t mla_decode_mtp_ex(mla_dtype_t dt, int b, int q_len, int h, int t_ma
     const WorkspaceLayout w = workspace_layout(b, rows, s.n_chunks, 2);
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
-    hipStream_t hs = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    int32_t* plan = (int32_t*)ws;
-    DecodeParams p;
-    p.q = q_prime;
-    p.cache = cache;
-    p.plan = plan;
-    p.out = out;
-    p.lse = lse;
-    p.plse = (float*)(ws + w.plse_off);
-    p.po = (void*)(ws + w.po_off);
-    p.block_table = nullptr;
-    p.cache_scale = nullptr;
-    p.seqlens = seqlens;
-    p.num_blocks = p.block_size = p.max_blocks = 0;
+    DecodeParams p = split_params(q_prime, cache, seqlens, out, lse, workspace, w, b, rows, t_max,
+                                  s.n_chunks, s.n_hg, softmax_scale);
     p.q_len = q_len;
     p.heads_per_token = h;
-    p.b = b;
-    p.h = rows;
-    p.t_max = t_max;
-    p.n_chunks = s.n_chunks;
-    p.n_hg = s.n_hg;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
-    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
-    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(seqlens, b, rows, t_max, s.n_chunks, 32, 1, plan, true, out, lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = s.nw == 4   ? launch_decode_wide_causal<4, 2>(p, hs)
-        : s.nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
-                    : launch_decode_wide_causal<1, 3>(p, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_combine(true, plan, b, rows, p.plse, p.po, out, lse, hs);
-    return hip_status(e);
+    return run_split(p, true, 32, 1, cfg, (hipStream_t)stream, [&] { return launch_mtp(p, s.nw, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, const void* q_prime,
@@ -418,43 +416,15 @@ mla_status_t mla_decode_paged_ex(mla_dtype_t dt, int b, int h, const void* q_pri
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
     const int t_max = max_blocks * block_size;
 
-    hipStream_t hs = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    int32_t* plan = (int32_t*)ws;
-    DecodeParams p;
-    p.q = q_prime;
-    p.cache = kv_pool;
-    p.plan = plan;
-    p.out = out;
-    p.lse = lse;
-    p.plse = (float*)(ws + w.plse_off);
-    p.po = (void*)(ws + w.po_off);
+    DecodeParams p = split_params(q_prime, kv_pool, seqlens, out, lse, workspace, w, b, h, t_max,
+                                  s.n_chunks, s.n_hg, softmax_scale);
     p.block_table = block_table;
-    p.cache_scale = nullptr;
-    p.seqlens = seqlens;
     p.num_blocks = num_blocks;
     p.block_size = block_size;
     p.max_blocks = max_blocks;
-    p.q_len = 1;
-    p.heads_per_token = h;
-    p.b = b;
-    p.h = h;
-    p.t_max = t_max;
-    p.n_chunks = s.n_chunks;
-    p.n_hg = s.n_hg;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
-    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
-    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
     // tile-aligned plan: every segment starts at a multiple of 32 tokens
-    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, 32, 32, plan, true, out, lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_decode_bf16(p, s.hpg, s.variant, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_combine(true, plan, b, h, p.plse, p.po, out, lse, hs);
-    return hip_status(e);
+    return run_split(p, true, 32, 32, cfg, (hipStream_t)stream,
+                     [&] { return launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_paged(mla_dtype_t dt, int b, int h, const void* q_prime, const void* kv_pool,
@@ -512,41 +482,11 @@ mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, con
     const WorkspaceLayout w = workspace_layout(b, h, s.n_chunks, 2);
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
-    hipStream_t hs = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    int32_t* plan = (int32_t*)ws;
-    DecodeParams p;
-    p.q = q_prime;
-    p.cache = cache_codes;
-    p.plan = plan;
-    p.out = out;
-    p.lse = lse;
-    p.plse = (float*)(ws + w.plse_off);
-    p.po = (void*)(ws + w.po_off);
-    p.block_table = nullptr;
+    DecodeParams p = split_params(q_prime, cache_codes, seqlens, out, lse, workspace, w, b, h, t_max,
+                                  s.n_chunks, s.n_hg, softmax_scale);
     p.cache_scale = cache_scale;
-    p.seqlens = seqlens;
-    p.num_blocks = p.block_size = p.max_blocks = 0;
-    p.q_len = 1;
-    p.heads_per_token = h;
-    p.b = b;
-    p.h = h;
-    p.t_max = t_max;
-    p.n_chunks = s.n_chunks;
-    p.n_hg = s.n_hg;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
-    hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
-    hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(seqlens, b, h, t_max, s.n_chunks, s.min_chunk, 1, plan, true, out,
-                               lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_decode_bf16(p, s.hpg, s.variant, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
-    e = launch_combine(true, plan, b, h, p.plse, p.po, out, lse, hs);
-    return hip_status(e);
+    return run_split(p, true, s.min_chunk, 1, cfg, (hipStream_t)stream,
+                     [&] { return launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_fp8(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
@@ -664,41 +604,16 @@ mla_status_t mla_decode_mtp_paged(mla_dtype_t dt, int b, int q_len, int h, const
     if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
     const int t_max = max_blocks * block_size;
 
-    hipStream_t hs = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    int32_t* plan = (int32_t*)ws;
-    DecodeParams p;
-    p.q = q_prime;
-    p.cache = kv_pool;
-    p.plan = plan;
-    p.out = out;
-    p.lse = lse;
-    p.plse = (float*)(ws + w.plse_off);
-    p.po = (void*)(ws + w.po_off);
+    DecodeParams p = split_params(q_prime, kv_pool, seqlens, out, lse, workspace, w, b, rows, t_max,
+                                  s.n_chunks, s.n_hg, softmax_scale);
     p.block_table = block_table;
-    p.cache_scale = nullptr;
-    p.seqlens = seqlens;
     p.num_blocks = num_blocks;
     p.block_size = block_size;
     p.max_blocks = max_blocks;
     p.q_len = q_len;
     p.heads_per_token = h;
-    p.b = b;
-    p.h = rows;
-    p.t_max = t_max;
-    p.n_chunks = s.n_chunks;
-    p.n_hg = s.n_hg;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
     // tile-aligned plan: every segment starts at a multiple of 32 tokens
-    hipError_t e = launch_plan(seqlens, b, rows, t_max, s.n_chunks, 32, 32, plan, true, out, lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    e = s.nw == 4   ? launch_decode_wide_causal<4, 2>(p, hs)
-        : s.nw == 2 ? launch_decode_wide_causal<2, 2>(p, hs)
-                    : launch_decode_wide_causal<1, 3>(p, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    e = launch_combine(true, plan, b, rows, p.plse, p.po, out, lse, hs);
-    return hip_status(e);
+    return run_split(p, true, 32, 32, nullptr, (hipStream_t)stream, [&] { return launch_mtp(p, s.nw, (hipStream_t)stream); });
 }
 
 mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,
@@ -711,3 +626,4 @@ mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const voi
 }
 
 }  // extern "C"
+#pragma GCC visibility pop
