@@ -38,6 +38,19 @@ def test_library_exports_every_declared_symbol(mla):
     assert set(_declared_functions()) == set(mla.EXPORTED_SYMBOLS)
 
 
+def test_library_exports_nothing_but_the_c_abi(mla):
+    # dynamic symbols the library defines (functions): exactly the header's
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    res = subprocess.run([nm, "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True,
+                         check=True)
+    funcs = {ln.split()[-1] for ln in res.stdout.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    assert funcs == set(_declared_functions()), sorted(funcs ^ set(_declared_functions()))
+
+
 def test_abi_version_and_status_strings(mla):
     assert mla.abi_version() == 1
     assert mla.status_string(0) == "ok"
