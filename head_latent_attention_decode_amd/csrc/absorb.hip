@@ -149,6 +149,22 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
 // rope[m][h][0:64] to y[...][ND:ND+64].
 // blk: this workgroup's index among the product's H * ND / (64 NCB) blocks;
 // OutT: type of Y (bf16, or fp32 for partial sums that are added up later).
+// Block index for workgroup id `id` of `count` when each head has NB blocks
+// that read the same input rows.  Workgroups go to the 8 XCDs round-robin by
+// id, so ids that are equal mod 8 share one XCD and its L2: head 8a + x gets
+// the ids 8 NB a + 8 j + x (its block j), and its input rows come from HBM
+// once rather than NB times.  Ids past the last whole group of 8 heads keep
+// their own index.
+template <int NB>
+__device__ __forceinline__ int xcd_head_block(int id, int count)
+{
+    constexpr int kSpan = 8 * NB;
+    const int full = count / kSpan * kSpan;
+    if (id >= full) return id;
+    const int a = id / kSpan, rem = id % kSpan;
+    return (8 * a + rem % 8) * NB + rem / 8;
+}
+
 template <int KD, int ND, int NCB, typename OutT>
 __device__ __forceinline__ void absorb_mfma_body(int blk, int M, int H, const __bf16* __restrict__ x,
                                                  long x_rs, const __bf16* __restrict__ w,
@@ -282,7 +298,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __
                                                           __bf16* __restrict__ y, long y_rs, int y_hs,
                                                           const __bf16* __restrict__ rope)
 {
-    absorb_mfma_body<KD, ND, NCB, __bf16>(blockIdx.x, M, H, x, x_rs, w, y, y_rs, y_hs, rope);
+    absorb_mfma_body<KD, ND, NCB, __bf16>(xcd_head_block<ND / (64 * NCB)>(blockIdx.x, gridDim.x), M, H, x,
+                                          x_rs, w, y, y_rs, y_hs, rope);
 }
 
 // ---- appending a token's latent row ------------------------------------------
@@ -308,8 +325,8 @@ __global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __
     const long x_rs = (long)H * kAppendKD;
     const int dkv_blocks = H * (kDc / 64);
     if ((int)blockIdx.x < dkv_blocks)
-        absorb_mfma_body<kAppendKD, kDc, 1, float>(blockIdx.x, M, H, x, x_rs, w_dkv, part,
-                                                   (long)H * kDqk, kDqk, nullptr);
+        absorb_mfma_body<kAppendKD, kDc, 1, float>(xcd_head_block<kDc / 64>(blockIdx.x, dkv_blocks), M, H, x,
+                                                   x_rs, w_dkv, part, (long)H * kDqk, kDqk, nullptr);
     else
         absorb_mfma_body<kAppendKD, kDr, 1, float>(blockIdx.x - dkv_blocks, M, H, x, x_rs, w_kr,
                                                    part + kDc, (long)H * kDqk, kDqk, nullptr);
