@@ -127,20 +127,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 
-__device__ inline void load8(const float* p, float (&x)[8])
-{
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 c = reinterpret_cast<const float4*>(p)[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
-}
+typedef float f32x8_v __attribute__((ext_vector_type(8)));
 
-__device__ inline void load8(const __bf16* p, float (&x)[8])
-{
-    const bf16x8_v v = *reinterpret_cast<const bf16x8_v*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
-}
+// Eight consecutive elements of a partial row as loaded (one 16- or 32-byte
+// load); they are converted to fp32 only where they are used, which keeps
+// the bf16 rows in flight at four registers each.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<__bf16> {
+    typedef bf16x8_v type;
+};
+template <>
+struct Vec8<float> {
+    typedef f32x8_v type;
+};
 
 __device__ inline void store8(float* p, const float (&x)[8])
 {
@@ -160,10 +161,12 @@ constexpr int kCombineThreads = 256;  // 4 waves = 4 heads of one batch row
 constexpr int kCombineUnroll = 8;     // partial rows in flight per wave
 
 // One wave per (batch row, head) of a row cut into several segments; no LDS
-// and no barrier.  Lane j first holds the lse of slots j, j+64, ... (max and
-// sum by shuffles), then every partial row (512 columns) is one coalesced
-// load, lane l taking columns 8l .. 8l+7, kCombineUnroll rows in flight; the
-// weight of slot s is read from the lane that holds it.  Rows with one
+// and no barrier.  Every partial row (512 columns) is one coalesced load,
+// lane l taking columns 8l .. 8l+7.  The slots are taken kCombineUnroll at a
+// time with a running max m, running sum l and unnormalised sum acc (the
+// usual online log-sum-exp): each round requests its slots' lse values
+// together with their partial rows, so a row with up to kCombineUnroll
+// segments waits on memory once after reading the plan.  Rows with one
 // segment were finished by the decode kernel, rows with none by plan_kernel.
 template <typename OutT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t* __restrict__ plan,
@@ -176,58 +179,63 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t*
     PlanView v{const_cast<int32_t*>(plan), b};
     const int groups = (h + 3) / 4;
     const int r = blockIdx.x / groups;
-    const int head = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
+    // the head is the same for the whole wave: keep it, and every address
+    // built on it but the lane's 16 bytes, in scalar registers
+    const int head = __builtin_amdgcn_readfirstlane((blockIdx.x % groups) * 4 + (threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (head >= h) return;
     const int ns = v.nsplit()[r];
     if (ns <= 1) return;
     const int s0 = v.base()[r];
     const float* pl = plse + (size_t)s0 * h + head;
+    const OutT* prow = po + ((size_t)s0 * h + head) * kDc;
 
-    float m = -INFINITY;
-    for (int s = lane; s < ns; s += 64) m = fmaxf(m, pl[(size_t)s * h]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (m == -INFINITY) {
-        // no segment saw a token (a causal query row with an empty prefix)
-        float z[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = 0.f;
-        store8(out + ((size_t)r * h + head) * kDc + 8 * lane, z);
-        if (lane == 0) lse[(size_t)r * h + head] = -INFINITY;
-        return;
-    }
-    float sm = 0.f;
-    for (int s = lane; s < ns; s += 64) sm += expf(pl[(size_t)s * h] - m);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off, 64);
-    const float inv = 1.0f / sm;
-
+    float m = -INFINITY, l = 0.f;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int sb = 0; sb < ns; sb += 64) {
-        // normalised weight of slot sb + lane, held by that lane
-        const float wl = sb + lane < ns ? expf(pl[(size_t)(sb + lane) * h] - m) * inv : 0.f;
-        const int nb = min(64, ns - sb);
-        for (int s = 0; s < nb; s += kCombineUnroll) {
-            float x[kCombineUnroll][8];
+    for (int s = 0; s < ns; s += kCombineUnroll) {
+        // slots past the end re-read the last one and take no part below
+        float ls[kCombineUnroll];
+        typename Vec8<OutT>::type x[kCombineUnroll];
 #pragma unroll
-            for (int u = 0; u < kCombineUnroll; ++u) {
-                const int sl = sb + min(s + u, nb - 1);
-                load8(po + ((size_t)(s0 + sl) * h + head) * kDc + 8 * lane, x[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < kCombineUnroll; ++u) {
-                // slots past the end re-read the last one with weight 0
-                const float w = s + u < nb ? __shfl(wl, s + u, 64) : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += w * x[u][e];
-            }
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int sl = min(s + u, ns - 1);
+            ls[u] = pl[(size_t)sl * h];
+            x[u] = reinterpret_cast<const typename Vec8<OutT>::type*>(prow + (size_t)sl * h * kDc)[lane];
         }
+        float mb = m;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u)
+            if (s + u < ns) mb = fmaxf(mb, ls[u]);
+        if (mb == -INFINITY) continue;  // no segment so far saw a token
+        const float scale = expf(m - mb);  // 0 while m is still -inf
+        l *= scale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= scale;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const float w = s + u < ns ? expf(ls[u] - mb) : 0.f;
+            l += w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[u][e];
+        }
+        m = mb;
     }
-    store8(out + ((size_t)r * h + head) * kDc + 8 * lane, acc);
-    if (lane == 0) lse[(size_t)r * h + head] = m + logf(sm);
+    OutT* o = out + ((size_t)r * h + head) * kDc + 8 * lane;
+    if (m == -INFINITY) {
+        // no segment saw a token (a causal query row with an empty prefix)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        store8(o, acc);
+        if (lane == 0) lse[(size_t)r * h + head] = -INFINITY;
+        return;
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    store8(o, acc);
+    if (lane == 0) lse[(size_t)r * h + head] = m + logf(l);
 }
 
 }  // namespace
