@@ -170,6 +170,8 @@ DecodeParams split_params(const void* q_prime, const void* cache, const int32_t*
     p.num_blocks = p.block_size = p.max_blocks = 0;
     p.q_len = 1;
     p.heads_per_token = rows;
+    p.plan_in_kernel = p.plan_min_chunk = 0;
+    p.plan_align = 1;
     p.b = b;
     p.h = rows;
     p.t_max = t_max;
@@ -182,17 +184,25 @@ DecodeParams split_params(const void* q_prime, const void* cache, const int32_t*
 // plan -> attention kernel -> combine on `hs`, with the caller's profiling
 // events (if any) recorded right before and after the attention kernel.
 // align > 1 lays the plan over lengths rounded up to whole tiles (paged pool).
+// kernel_plans: the attention kernel can build the plan itself; it does when
+// the plan fits its LDS, and no plan kernel is launched.  `kernel` is called
+// with the final parameters.
 template <typename Kernel>
-mla_status_t run_split(const DecodeParams& p, bool bf16, int min_chunk, int align,
+mla_status_t run_split(DecodeParams p, bool bf16, int min_chunk, int align, bool kernel_plans,
                        const mla_decode_config_t* cfg, hipStream_t hs, Kernel&& kernel)
 {
     hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
     hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
-    hipError_t e = launch_plan(p.seqlens, p.b, p.h, p.t_max, p.n_chunks, min_chunk, align,
-                               const_cast<int32_t*>(p.plan), bf16, p.out, p.lse, hs);
-    if (e != hipSuccess) return MLA_ERR_HIP;
+    p.plan_in_kernel = kernel_plans && p.b <= kPlanLdsRows && p.n_chunks <= kPlanLdsChunks;
+    p.plan_min_chunk = min_chunk;
+    p.plan_align = align;
+    if (!p.plan_in_kernel) {
+        hipError_t e = launch_plan(p.seqlens, p.b, p.h, p.t_max, p.n_chunks, min_chunk, align,
+                                   const_cast<int32_t*>(p.plan), bf16, p.out, p.lse, hs);
+        if (e != hipSuccess) return MLA_ERR_HIP;
+    }
     if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
-    if (kernel() != hipSuccess) return MLA_ERR_HIP;
+    if (kernel(p) != hipSuccess) return MLA_ERR_HIP;
     if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
     return hip_status(launch_combine(bf16, p.plan, p.b, p.h, p.plse, p.po, p.out, p.lse, hs));
 }
@@ -260,9 +270,10 @@ mla_status_t mla_decode_ex(mla_dtype_t dt, int b, int h, int t_max, const void* 
     const bool bf16 = dt == MLA_DTYPE_BF16;
     DecodeParams p = split_params(q_prime, cache, seqlens, out, lse, workspace, w, b, h, t_max,
                                   s.n_chunks, s.n_hg, softmax_scale);
-    return run_split(p, bf16, s.min_chunk, 1, cfg, (hipStream_t)stream, [&] {
-        return bf16 ? launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream)
-                    : launch_decode_f32(p, (hipStream_t)stream);
+    const bool plans = bf16 && bf16_variant_plans(s.hpg, s.variant);
+    return run_split(p, bf16, s.min_chunk, 1, plans, cfg, (hipStream_t)stream, [&](const DecodeParams& q) {
+        return bf16 ? launch_decode_bf16(q, s.hpg, s.variant, (hipStream_t)stream)
+                    : launch_decode_f32(q, (hipStream_t)stream);
     });
 }
 
@@ -362,7 +373,8 @@ mla_status_t mla_decode_mtp_ex(mla_dtype_t dt, int b, int q_len, int h, int t_ma
                                   s.n_chunks, s.n_hg, softmax_scale);
     p.q_len = q_len;
     p.heads_per_token = h;
-    return run_split(p, true, 32, 1, cfg, (hipStream_t)stream, [&] { return launch_mtp(p, s.nw, (hipStream_t)stream); });
+    return run_split(p, true, 32, 1, true, cfg, (hipStream_t)stream,
+                     [&](const DecodeParams& q) { return launch_mtp(q, s.nw, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_mtp(mla_dtype_t dt, int b, int q_len, int h, int t_max, const void* q_prime,
@@ -423,8 +435,8 @@ mla_status_t mla_decode_paged_ex(mla_dtype_t dt, int b, int h, const void* q_pri
     p.block_size = block_size;
     p.max_blocks = max_blocks;
     // tile-aligned plan: every segment starts at a multiple of 32 tokens
-    return run_split(p, true, 32, 32, cfg, (hipStream_t)stream,
-                     [&] { return launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream); });
+    return run_split(p, true, 32, 32, bf16_variant_plans(s.hpg, s.variant), cfg, (hipStream_t)stream,
+                     [&](const DecodeParams& q) { return launch_decode_bf16(q, s.hpg, s.variant, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_paged(mla_dtype_t dt, int b, int h, const void* q_prime, const void* kv_pool,
@@ -485,8 +497,8 @@ mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, con
     DecodeParams p = split_params(q_prime, cache_codes, seqlens, out, lse, workspace, w, b, h, t_max,
                                   s.n_chunks, s.n_hg, softmax_scale);
     p.cache_scale = cache_scale;
-    return run_split(p, true, s.min_chunk, 1, cfg, (hipStream_t)stream,
-                     [&] { return launch_decode_bf16(p, s.hpg, s.variant, (hipStream_t)stream); });
+    return run_split(p, true, s.min_chunk, 1, false, cfg, (hipStream_t)stream,
+                     [&](const DecodeParams& q) { return launch_decode_bf16(q, s.hpg, s.variant, (hipStream_t)stream); });
 }
 
 mla_status_t mla_decode_fp8(int b, int h, int t_max, const void* q_prime, const void* cache_codes,
@@ -613,7 +625,8 @@ mla_status_t mla_decode_mtp_paged(mla_dtype_t dt, int b, int q_len, int h, const
     p.q_len = q_len;
     p.heads_per_token = h;
     // tile-aligned plan: every segment starts at a multiple of 32 tokens
-    return run_split(p, true, 32, 32, nullptr, (hipStream_t)stream, [&] { return launch_mtp(p, s.nw, (hipStream_t)stream); });
+    return run_split(p, true, 32, 32, true, nullptr, (hipStream_t)stream,
+                     [&](const DecodeParams& q) { return launch_mtp(q, s.nw, (hipStream_t)stream); });
 }
 
 mla_status_t mla_absorb_o(mla_dtype_t dt, int b, int h, const void* o, const void* w_uv, void* y,

@@ -972,43 +972,44 @@ struct VariantEntry {
     const char* paged_name;  // the same for a paged cache; nullptr: not supported
     hipError_t (*launch_fp8)(const DecodeParams&, hipStream_t);  // fp8 cache; nullptr: none
     const char* fp8_name;
+    bool plans;  // builds its own split plan in LDS (wide kernels with LDS to spare)
 };
 
 // heads_per_group, variant id, tile tokens, launcher, names, fp8 launcher and name
 const VariantEntry kVariants[] = {
     {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, false>", nullptr,
-     &launch_variant_fp8<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, true>"},
+     &launch_variant_fp8<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, true>", false},
     {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>, "decode_bf16_kernel<16, 1, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>, "decode_bf16_kernel<16, 2, 2, 32, 2, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>, "decode_bf16_kernel<32, 1, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>, "decode_bf16_kernel<16, 4, 1, 64, 2, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>, "decode_bf16_kernel<32, 2, 1, 32, 4, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>, "decode_bf16_kernel<32, 4, 1, 32, 4, false>", nullptr,
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>, "decode_bf16_kernel<16, 8, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr},
-    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>", nullptr, nullptr, nullptr},
+     nullptr, nullptr, false},
+    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>", nullptr, nullptr, nullptr, false},
     // The three-stage ring (pair kernel <2, 3>) is switched off: it took a GPU
     // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
     // cause has not been found; every other variant passes the same tests.
-    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>", nullptr, nullptr, nullptr},
+    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>", nullptr, nullptr, nullptr, false},
     {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3, false>", "decode_wide_kernel<4, 3, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, true},
     {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2, false>", "decode_wide_kernel<4, 2, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, true},
     {128, 5, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4, false>", "decode_wide_kernel<4, 4, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, false},
     {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3, false>", "decode_wide_kernel<2, 3, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, true},
     {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2, false>", "decode_wide_kernel<2, 2, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, true},
     {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3, false>", "decode_wide_kernel<1, 3, true>",
-     nullptr, nullptr},
+     nullptr, nullptr, true},
 };
 
 const VariantEntry* find_variant(int hpg, int variant)
@@ -1042,6 +1043,12 @@ const char* fp8_kernel_name(int heads_per_group, int variant)
 {
     const VariantEntry* v = find_variant(heads_per_group, variant);
     return v == nullptr ? nullptr : v->fp8_name;
+}
+
+bool bf16_variant_plans(int heads_per_group, int variant)
+{
+    const VariantEntry* v = find_variant(heads_per_group, variant);
+    return v != nullptr && v->plans;
 }
 
 bool bf16_variant_pages(int heads_per_group, int variant)

@@ -34,6 +34,7 @@
 //  * Online softmax in base 2, lazy rescale (only when the running max grows
 //    by more than 2^8), exact final normalisation.
 #include "bf16_common.h"
+#include "plan_build.h"
 
 #include <math.h>
 
@@ -71,6 +72,8 @@ struct WideTiling {
     static_assert(STAGES * TILE_BYTES <= 160 * 1024, "LDS budget");
     static_assert((STAGES - 2) * LOADS <= 63, "vmcnt range");
     static_assert(LOADS <= KS, "refill spread over the score steps");
+    // room in LDS for the workgroup's own copy of the split plan
+    static constexpr bool PLANS = STAGES * TILE_BYTES + kPlanLdsInts * 4 <= 160 * 1024;
 };
 
 // Scalar (constant address space) view of device data that no kernel writes
@@ -96,13 +99,51 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
 
     int k, hg;
     block_work(p.n_chunks, p.n_hg, k, hg);
-    const PlanView pv{const_cast<int32_t*>(p.plan), p.b};
-    // plan entries are the same for every lane: keep them in scalar registers
-    auto plan_at = [](const int32_t* q) { return __builtin_amdgcn_readfirstlane(*q); };
-    const int total = plan_at(p.plan);
-    const int chunk = plan_at(p.plan + 1);
-    int r = plan_at(pv.chunk_row() + k);
-    if (r < 0) return;
+    // The split plan: plan_kernel's copy in the workspace or, with
+    // plan_in_kernel, this workgroup's own copy in LDS, built by wave 0 from
+    // seqlens (one load of the lengths instead of a kernel launch and two
+    // dependent plan loads).  Entries are the same for every lane: they are
+    // kept in scalar registers.
+    __shared__ int32_t lplan[T::PLANS ? kPlanLdsInts : 1];
+    const bool lds_plan = p.plan_in_kernel != 0;
+    if (lds_plan) {
+        if (!T::PLANS) return;  // the host never asks this of a kernel without the LDS for it
+        if (wave == 0)
+            build_plan(p.seqlens, p.b, p.t_max, p.n_chunks, p.plan_min_chunk, p.plan_align,
+                       (LDS_AS int32_t*)lplan);
+        __syncthreads();
+        // The combine reads the plan from the workspace: workgroup 0 leaves it
+        // there.  These stores go out before any tile DMA, so they only make
+        // the tile waits below (which count outstanding vector-memory
+        // operations) more conservative.
+        if (blockIdx.x == 0) {
+            const int n = 4 + (p.b + 1) + 2 * p.b + p.n_chunks;
+            for (int i = threadIdx.x; i < n; i += T::THREADS)
+                const_cast<int32_t*>(p.plan)[i] = ((const LDS_AS int32_t*)lplan)[i];
+        }
+    }
+    auto pl = [&](int idx) {
+        return __builtin_amdgcn_readfirstlane(lds_plan ? ((const LDS_AS int32_t*)lplan)[idx] : p.plan[idx]);
+    };
+    auto pl_cu = [&](int row) { return pl(4 + row); };
+    auto pl_base = [&](int row) { return pl(4 + (p.b + 1) + row); };
+    auto pl_nsplit = [&](int row) { return pl(4 + (p.b + 1) + p.b + row); };
+    auto seqlen_of = [&](int row) { return __builtin_amdgcn_readfirstlane(p.seqlens[row]); };
+    // With its own plan, every workgroup also takes its share of the plan
+    // kernel's other duty once its segments are done: rows with no tokens
+    // (lengths read from the plan) get out = 0, lse = -inf.
+    auto plan_duties = [&]() {
+        if (!lds_plan) return;
+        zero_empty_rows([&](int row) { return pl_cu(row + 1) - pl_cu(row); }, p.b, p.h, (__bf16*)p.out, p.lse,
+                        blockIdx.x, gridDim.x, threadIdx.x, T::THREADS);
+    };
+    const int total = pl(0);
+    const int chunk = pl(1);
+    int r = pl(4 + (p.b + 1) + 2 * p.b + k);
+    if (r < 0) {
+        plan_duties();
+        return;
+    }
     int pos = k * chunk;
     const int end = pos + min(chunk, total - pos);
 
@@ -147,26 +188,26 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
     }
 
     while (true) {
-        const int row_lo = plan_at(pv.cu() + r);
-        const int row_hi = plan_at(pv.cu() + r + 1);
+        const int row_lo = pl_cu(r);
+        const int row_hi = pl_cu(r + 1);
         const int seg_end = min(end, row_hi);
         const int seg_a = pos - row_lo;
         int seg_len = seg_end - pos;
         if (PAGED) {
             // the plan covers lengths rounded up to whole tiles: mask the rest
-            const int L = min(max(plan_at(p.seqlens + r), 0), p.t_max);
+            const int L = min(max(seqlen_of(r), 0), p.t_max);
             seg_len = max(0, min(seg_len, L - seg_a));
         }
         // CAUSAL: tokens of this segment the lane's query row may see (any
         // value: <= 0 none, >= seg_len all)
         int c_lim = 0;
         if constexpr (CAUSAL) {
-            const int L = PAGED ? min(max(plan_at(p.seqlens + r), 0), p.t_max) : row_hi - row_lo;
+            const int L = PAGED ? min(max(seqlen_of(r), 0), p.t_max) : row_hi - row_lo;
             c_lim = L - p.q_len + 1 + head / p.heads_per_token - seg_a;
         }
         const int split_j = k - row_lo / chunk;
-        const bool final_out = plan_at(pv.nsplit() + r) == 1;
-        const int slot = plan_at(pv.base() + r) + split_j;
+        const bool final_out = pl_nsplit(r) == 1;
+        const int slot = pl_base(r) + split_j;
         const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
         const int n_tiles = (seg_len + T::N - 1) / T::N;
 
@@ -445,8 +486,9 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         if (pos >= end) break;
         wg_barrier();  // every wave is done with the stages before they are refilled
         ++r;
-        while (plan_at(pv.cu() + r + 1) <= pos) ++r;
+        while (pl_cu(r + 1) <= pos) ++r;
     }
+    plan_duties();
 }
 
 template <int NW, int STAGES, bool PAGED>

@@ -91,7 +91,18 @@ struct DecodeParams {
     int n_chunks;         // chunks per head group
     int n_hg;             // head groups
     float scale_log2;     // softmax_scale * log2(e)
+    // plan_in_kernel != 0 (wide kernels only): no plan kernel ran; every
+    // workgroup builds the plan in LDS from seqlens (with plan_min_chunk and
+    // plan_align), workgroup 0 leaves a copy at `plan` for the combine, and
+    // the attention kernel gives rows with no tokens out = 0, lse = -inf.
+    int plan_in_kernel, plan_min_chunk, plan_align;
 };
+
+// Largest batch and chunk count whose plan an attention workgroup builds in
+// its own LDS (11 KB); larger ones go through plan_kernel.
+constexpr int kPlanLdsRows = 256;
+constexpr int kPlanLdsChunks = 2048;
+constexpr int kPlanLdsInts = 4 + (kPlanLdsRows + 1) + 2 * kPlanLdsRows + kPlanLdsChunks;
 
 // Launchers (return hipGetLastError() after the launch).
 // launch_plan also writes out = 0, lse = -inf for every row with no tokens
@@ -115,6 +126,8 @@ const char* bf16_kernel_name(int heads_per_group, int variant, bool paged);
 bool bf16_variant_pages(int heads_per_group, int variant);  // has a paged-cache form
 // fp8 latent cache: only some variants have a form that reads e4m3 codes
 bool bf16_variant_fp8(int heads_per_group, int variant);
+// the variant builds its split plan itself (plan_in_kernel may be set)
+bool bf16_variant_plans(int heads_per_group, int variant);
 const char* fp8_kernel_name(int heads_per_group, int variant);
 hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
                               hipStream_t stream);

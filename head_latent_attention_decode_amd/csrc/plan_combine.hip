@@ -8,6 +8,7 @@
 // score parts are summed; the Polish glossary notes attention parallelises over
 // tokens.  The split itself is this library's scheduling choice.
 #include "mla355_internal.h"
+#include "plan_build.h"
 
 #include <math.h>
 
@@ -17,112 +18,21 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanMaxRowBlocks = 2048;
 
-// Inclusive scan across the 64 lanes of a wave.
-__device__ int wave_inclusive_scan(int x)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-__device__ int clamped_len(const int32_t* seqlens, int i, int t_max)
-{
-    const int L = seqlens[i];
-    return L < 0 ? 0 : (L > t_max ? t_max : L);
-}
-
-// Workgroup 0, wave 0 builds the plan (two scans over the clamped lengths, 64
-// rows per step).  Workgroups 1.. give every row with no tokens out = 0 and
-// lse = -inf.  With align > 1 the plan is laid over the lengths rounded up to
-// a multiple of align, and the chunk too, so that every segment starts at a
-// multiple of align inside its row (the paged cache needs whole tiles inside
-// one block); the kernel masks the padding with the true lengths.
+// Workgroup 0, wave 0 builds the plan; workgroups 1.. give every row with no
+// tokens out = 0 and lse = -inf.
 template <typename OutT>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
                                                             int b, int h, int t_max, int n_chunks,
                                                             int min_chunk, int align, int32_t* plan,
                                                             OutT* out, float* lse)
 {
-    auto planned_len = [&](int i) { return (clamped_len(seqlens, i, t_max) + align - 1) / align * align; };
-    const int tid = threadIdx.x;
     if (blockIdx.x > 0) {
-        for (int r = blockIdx.x - 1; r < b; r += gridDim.x - 1) {
-            if (clamped_len(seqlens, r, t_max) != 0) continue;
-            OutT* o = out + (size_t)r * h * kDc;
-            for (int i = tid; i < h * kDc; i += kPlanThreads) o[i] = (OutT)0.f;
-            for (int i = tid; i < h; i += kPlanThreads) lse[(size_t)r * h + i] = -INFINITY;
-        }
+        zero_empty_rows([&](int r) { return clamped_len(seqlens, r, t_max); }, b, h, out, lse, blockIdx.x - 1,
+                        gridDim.x - 1, threadIdx.x, kPlanThreads);
         return;
     }
-    if (tid >= 64) return;
-    PlanView v{plan, b};
-    const int lane = tid;
-
-    // Pass 1: cu[] = prefix sums of the clamped lengths.
-    int carry = 0;
-    if (lane == 0) v.cu()[0] = 0;
-    for (int base = 0; base < b; base += 64) {
-        const int i = base + lane;
-        const int L = i < b ? planned_len(i) : 0;
-        const int inc = wave_inclusive_scan(L);
-        if (i < b) v.cu()[i + 1] = carry + inc;
-        carry += __shfl(inc, 63, 64);
-    }
-    const int total = carry;
-    int chunk = (int)(((long long)total + n_chunks - 1) / n_chunks);
-    if (chunk < min_chunk) chunk = min_chunk;
-    chunk = (chunk + align - 1) / align * align;
-    if (lane == 0) {
-        plan[0] = total;
-        plan[1] = chunk;
-        plan[2] = n_chunks;
-        plan[3] = 0;
-    }
-    // Chunks starting at or past the last token are idle.  Every other chunk
-    // k starts inside exactly one non-empty row (the one holding token
-    // k * chunk), written in pass 2; the two sets are disjoint.
-    const int first_idle = (total + chunk - 1) / chunk;
-    for (int k = first_idle + lane; k < n_chunks; k += 64) v.chunk_row()[k] = -1;
-
-    // Pass 2 (the lengths are scanned again rather than read back): segments
-    // per row, first partial slot per row, and the starting row of every chunk.
-    carry = 0;
-    int slots = 0;
-    for (int base = 0; base < b; base += 64) {
-        const int i = base + lane;
-        const int L = i < b ? planned_len(i) : 0;
-        const int inc = wave_inclusive_scan(L);
-        const int hi = carry + inc, lo = hi - L;
-        int ns = 0, k_lo = 0, k_hi = 0;  // chunks k_lo .. k_hi-1 start inside row i
-        if (i < b && L > 0) {
-            ns = (hi - 1) / chunk - lo / chunk + 1;
-            k_lo = (int)(((long long)lo + chunk - 1) / chunk);
-            k_hi = (int)(((long long)hi + chunk - 1) / chunk);
-        }
-        // a lane writes its own row's few chunk starts; rows holding many are
-        // written by the whole wave, one row at a time
-        constexpr int kLaneChunks = 4;
-        if (k_hi - k_lo <= kLaneChunks)
-            for (int k = k_lo; k < k_hi; ++k) v.chunk_row()[k] = i;
-        unsigned long long many = __ballot(k_hi - k_lo > kLaneChunks);
-        while (many) {
-            const int j = __builtin_ctzll(many);
-            many &= many - 1;
-            const int a = __shfl(k_lo, j, 64), z = __shfl(k_hi, j, 64);
-            for (int k = a + lane; k < z; k += 64) v.chunk_row()[k] = base + j;
-        }
-        const int ns_inc = wave_inclusive_scan(ns);
-        if (i < b) {
-            v.nsplit()[i] = ns;
-            v.base()[i] = slots + ns_inc - ns;
-        }
-        carry += __shfl(inc, 63, 64);
-        slots += __shfl(ns_inc, 63, 64);
-    }
+    if (threadIdx.x >= 64) return;
+    build_plan(seqlens, b, t_max, n_chunks, min_chunk, align, plan);
 }
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));

@@ -96,7 +96,8 @@ def _case_id(c):
 @pytest.mark.parametrize("h,cfg", BF16_CASES, ids=[_case_id(c) for c in BF16_CASES])
 def test_bf16_edges_every_output(mla, h, cfg):
     w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=100 + h, device="cuda")
-    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
+    # 2560 chunks: more than a wide kernel plans in its own LDS (plan kernel)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}, {"n_chunks": 2560}):
         c = dict(cfg or {})
         c.update(extra)
         out, lse = _run(mla, w, c or None)
@@ -201,6 +202,7 @@ def _plan_model(lens, t_max, n_chunks, min_chunk):
     return [total, chunk, n_chunks, 0] + cu + base + ns + row_of
 
 
+@pytest.mark.parametrize("n_chunks", [256, 4096], ids=["in-kernel", "plan-kernel"])
 @pytest.mark.parametrize("lens", [
     [4096] * 64,                                    # uniform: four chunks per row
     [131072] * 4,                                   # long rows: 64 chunk starts per row
@@ -208,20 +210,28 @@ def _plan_model(lens, t_max, n_chunks, min_chunk):
     [0, 0, 0],                                      # nothing to attend
     [-3, 10**9, 40],                                # out-of-range lengths are clamped
 ], ids=["uniform", "long", "ragged", "empty", "clamped"])
-def test_plan_bit_exact(mla, lens):
-    # the plan sits at the start of the workspace; integer data, compared exactly
+def test_plan_bit_exact(mla, lens, n_chunks):
+    # The plan sits at the start of the workspace; integer data, compared
+    # exactly.  At 128 heads the attention kernel builds the plan itself when
+    # it fits its LDS (256 chunks here) and leaves a copy in the workspace;
+    # 4096 chunks go through the separate plan kernel.
     b, h = len(lens), 128
     t_max = min(max(max(lens), 1), 131072)
     cache = torch.zeros(b, t_max, 576, dtype=torch.bfloat16, device="cuda")
     q = torch.zeros(b, h, 576, dtype=torch.bfloat16, device="cuda")
     seqlens = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(mla.mla_decode_workspace_bytes(torch.bfloat16, b, h, t_max), dtype=torch.uint8,
+    cfg = {"n_chunks": n_chunks}
+    ws = torch.zeros(mla.mla_decode_workspace_bytes(torch.bfloat16, b, h, t_max, cfg), dtype=torch.uint8,
                      device="cuda")
-    mla.mla_decode(q, cache, seqlens, SCALE, workspace=ws)
+    out, lse = mla.mla_decode(q, cache, seqlens, SCALE, workspace=ws, config=cfg)
     torch.cuda.synchronize()
-    ref = _plan_model(lens, t_max, 256, 32)
+    ref = _plan_model(lens, t_max, n_chunks, 32)
     got = ws[:4 * len(ref)].cpu().view(torch.int32).tolist()
     assert got == ref
+    # empty rows are written by whichever kernel holds the plan
+    for i, L in enumerate(lens):
+        if min(max(L, 0), t_max) == 0:
+            assert torch.all(out[i] == 0) and torch.all(torch.isneginf(lse[i]))
 
 
 # ---------------------------------------------------------------- paged latent cache
@@ -450,17 +460,20 @@ def _mtp_workload(b, q_len, h, lens, seed):
 def test_mtp_every_output(mla, q_len, h, lens):
     b = len(lens)
     w, q = _mtp_workload(b, q_len, h, lens, seed=700 + q_len * h)
-    out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale)
-    torch.cuda.synchronize()
     ref_o, ref_l = oracle.decode_latent_causal(q.cpu(), w.cache.cpu(), w.seqlens.cpu().numpy(), w.scale)
-    assert_out(to_np(out), ref_o, BF16_OUT_REL)
-    assert_lse(to_np(lse), ref_l, BF16_LSE_ABS)
-    # tokens with nothing to attend to: exactly zero output
     n = np.clip(np.array(lens)[:, None] - q_len + 1 + np.arange(q_len)[None, :], 0, None)
-    for i in range(b):
-        for t in range(q_len):
-            if n[i, t] == 0:
-                assert torch.all(out[i, t] == 0) and torch.all(torch.isneginf(lse[i, t]))
+    # default schedule (the kernel builds its own plan) and 2560 chunks (too
+    # many for its LDS: the separate plan kernel)
+    for cfg in (None, {"n_chunks": 2560}):
+        out, lse = mla.mla_decode_mtp(q, w.cache, w.seqlens, w.scale, config=cfg)
+        torch.cuda.synchronize()
+        assert_out(to_np(out), ref_o, BF16_OUT_REL)
+        assert_lse(to_np(lse), ref_l, BF16_LSE_ABS)
+        # tokens with nothing to attend to: exactly zero output
+        for i in range(b):
+            for t in range(q_len):
+                if n[i, t] == 0:
+                    assert torch.all(out[i, t] == 0) and torch.all(torch.isneginf(lse[i, t]))
 
 
 def test_mtp_one_token_is_decode(mla):
