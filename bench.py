@@ -44,7 +44,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 # sources of the dominant (split-KV attention) kernel: the traffic figures in
 # TRAFFIC_FILE are only valid while these are unchanged
 KERNEL_SRCS = [os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", f)
-               for f in ("decode_wide.hip", "bf16_common.h", "mla355_internal.h")]
+               for f in ("decode_wide.hip", "bf16_common.h", "mla355_internal.h", "plan_build.h")]
 
 
 def log(*a):
