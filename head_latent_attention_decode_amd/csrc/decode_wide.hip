@@ -107,7 +107,7 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
     __shared__ int32_t lplan[T::PLANS ? kPlanLdsInts : 1];
     const bool lds_plan = p.plan_in_kernel != 0;
     if (lds_plan) {
-        if (!T::PLANS) return;  // the host never asks this of a kernel without the LDS for it
+        if (!T::PLANS) return;  // the launcher refuses this combination
         if (wave == 0)
             build_plan(p.seqlens, p.b, p.t_max, p.n_chunks, p.plan_min_chunk, p.plan_align,
                        (LDS_AS int32_t*)lplan);
@@ -509,6 +509,8 @@ template <int NW, int STAGES>
 hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream)
 {
     using T = WideTiling<NW, STAGES>;
+    if (p.plan_in_kernel && (!T::PLANS || p.b > kPlanLdsRows || p.n_chunks > kPlanLdsChunks))
+        return hipErrorInvalidValue;  // no room for the plan in this kernel's LDS
     const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
     if (p.block_table != nullptr)
         decode_wide_kernel<NW, STAGES, true><<<grid, T::THREADS, 0, stream>>>(p);
@@ -528,6 +530,8 @@ template <int NW, int STAGES>
 hipError_t launch_decode_wide_causal(const DecodeParams& p, hipStream_t stream)
 {
     using T = WideTiling<NW, STAGES>;
+    if (p.plan_in_kernel && (!T::PLANS || p.b > kPlanLdsRows || p.n_chunks > kPlanLdsChunks))
+        return hipErrorInvalidValue;  // no room for the plan in this kernel's LDS
     const unsigned grid = (unsigned)p.n_chunks * (unsigned)p.n_hg;
     if (p.block_table != nullptr)
         decode_wide_causal_kernel<NW, STAGES, true><<<grid, T::THREADS, 0, stream>>>(p);
