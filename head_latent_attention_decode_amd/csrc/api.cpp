@@ -204,7 +204,7 @@ mla_status_t run_split(DecodeParams p, bool bf16, int min_chunk, int align, bool
     if (ev0 && hipEventRecord(ev0, hs) != hipSuccess) return MLA_ERR_HIP;
     if (kernel(p) != hipSuccess) return MLA_ERR_HIP;
     if (ev1 && hipEventRecord(ev1, hs) != hipSuccess) return MLA_ERR_HIP;
-    return hip_status(launch_combine(bf16, p.plan, p.b, p.h, p.plse, p.po, p.out, p.lse, hs));
+    return hip_status(launch_combine(bf16, p.plan, p.b, p.h, p.n_chunks, p.plse, p.po, p.out, p.lse, hs));
 }
 
 }  // namespace

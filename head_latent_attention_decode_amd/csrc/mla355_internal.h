@@ -110,7 +110,9 @@ constexpr int kPlanLdsInts = 4 + (kPlanLdsRows + 1) + 2 * kPlanLdsRows + kPlanLd
 // lengths (and a chunk) rounded up to multiples of align (paged cache).
 hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
                        int align, int32_t* plan, bool bf16, void* out, float* lse, hipStream_t stream);
-hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
+// n_chunks picks the combine's layout (rows with many segments get a
+// workgroup per (row, head)); any value gives the same result.
+hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, int n_chunks, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream);
 
 // bf16 decode variants.  heads_per_group selects the family; variant picks a

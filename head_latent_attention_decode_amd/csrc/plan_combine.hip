@@ -148,6 +148,103 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t*
     if (lane == 0) lse[(size_t)r * h + head] = m + logf(l);
 }
 
+// Rows cut into many segments: one workgroup per (row, head).  Wave w takes
+// slots w, w + 4, w + 8, ... with the online log-sum-exp above
+// (kCombineUnroll of its slots per round), and the four (m, l, acc) are
+// merged through LDS by wave 0.
+template <typename OutT>
+__global__ __launch_bounds__(kCombineThreads) void combine_split_kernel(const int32_t* __restrict__ plan,
+                                                                        int b, int h,
+                                                                        const float* __restrict__ plse,
+                                                                        const OutT* __restrict__ po,
+                                                                        OutT* __restrict__ out,
+                                                                        float* __restrict__ lse)
+{
+    constexpr int NW = kCombineThreads / 64;
+    __shared__ float wm[NW], wl[NW];
+    __shared__ float wacc[NW][8 * 64];  // [wave][element * 64 + lane]
+    PlanView v{const_cast<int32_t*>(plan), b};
+    const int r = blockIdx.x / h;
+    const int head = blockIdx.x % h;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int ns = v.nsplit()[r];
+    if (ns <= 1) return;  // the same for the whole workgroup
+    const int s0 = v.base()[r];
+    const float* pl = plse + (size_t)s0 * h + head;
+    const OutT* prow = po + ((size_t)s0 * h + head) * kDc;
+
+    float m = -INFINITY, l = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int s = wave; s < ns; s += NW * kCombineUnroll) {
+        // this wave's slots s, s + NW, ...; past the end it re-reads slot s
+        // (weight 0 below)
+        float ls[kCombineUnroll];
+        typename Vec8<OutT>::type x[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int sl = s + NW * u < ns ? s + NW * u : s;
+            ls[u] = pl[(size_t)sl * h];
+            x[u] = reinterpret_cast<const typename Vec8<OutT>::type*>(prow + (size_t)sl * h * kDc)[lane];
+        }
+        float mb = m;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u)
+            if (s + NW * u < ns) mb = fmaxf(mb, ls[u]);
+        if (mb == -INFINITY) continue;
+        const float scale = expf(m - mb);
+        l *= scale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= scale;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const float w = s + NW * u < ns ? expf(ls[u] - mb) : 0.f;
+            l += w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[u][e];
+        }
+        m = mb;
+    }
+    if (lane == 0) {
+        wm[wave] = m;
+        wl[wave] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wacc[wave][e * 64 + lane] = acc[e];
+    __syncthreads();
+    if (wave != 0) return;
+
+    float mx = wm[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, wm[w]);
+    OutT* o = out + ((size_t)r * h + head) * kDc + 8 * lane;
+    if (mx == -INFINITY) {
+        // no segment saw a token (a causal query row with an empty prefix)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        store8(o, acc);
+        if (lane == 0) lse[(size_t)r * h + head] = -INFINITY;
+        return;
+    }
+    float lt = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float f = wm[w] == -INFINITY ? 0.f : expf(wm[w] - mx);
+        lt += wl[w] * f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += f * wacc[w][e * 64 + lane];
+    }
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    store8(o, acc);
+    if (lane == 0) lse[(size_t)r * h + head] = mx + logf(lt);
+}
+
 }  // namespace
 
 hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_chunks, int min_chunk,
@@ -163,9 +260,21 @@ hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_ch
     return hipGetLastError();
 }
 
-hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, const float* plse,
+hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, int n_chunks, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream)
 {
+    // Sixteen or more segments per row on average: a workgroup per (row, head)
+    // so that the slots are read four waves at a time.
+    if ((long long)n_chunks >= 16LL * b) {
+        const unsigned grid = (unsigned)b * (unsigned)h;
+        if (bf16)
+            combine_split_kernel<__bf16><<<grid, kCombineThreads, 0, stream>>>(plan, b, h, plse, (const __bf16*)po,
+                                                                               (__bf16*)out, lse);
+        else
+            combine_split_kernel<float><<<grid, kCombineThreads, 0, stream>>>(plan, b, h, plse, (const float*)po,
+                                                                              (float*)out, lse);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)b * (unsigned)((h + 3) / 4);
     if (bf16)
         combine_kernel<__bf16><<<grid, kCombineThreads, 0, stream>>>(plan, b, h, plse, (const __bf16*)po,
