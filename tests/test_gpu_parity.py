@@ -682,3 +682,29 @@ def test_large_batch_short_rows(mla, h):
     check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, rows)
     empty = (lens == 0).nonzero().flatten().tolist()
     assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+
+
+@pytest.mark.parametrize("b,n_chunks", [(256, 2048), (257, 2048), (256, 2056)],
+                         ids=["lds-plan-full", "rows-past-lds-plan", "chunks-past-lds-plan"])
+def test_wide_kernel_plan_limits(mla, b, n_chunks):
+    # At 128 heads the attention kernel builds the split plan in its LDS for up
+    # to 256 rows and 2048 chunks (256 x 2048 fills that array exactly); one
+    # row or one chunk group more and the separate plan kernel runs instead.
+    # Short rows, every seventh empty: each row is compared with the oracle
+    # and every empty row must be exactly zero on both sides of the limit.
+    h = 128
+    g = torch.Generator().manual_seed(130 + b + n_chunks)
+    lens = torch.randint(0, 300, (b,), generator=g)
+    lens[::7] = 0
+    w = workloads.make_custom(b, h, lens.tolist(), seed=131 + b, device="cuda")
+    cfg = {"n_chunks": n_chunks}
+    ws = torch.zeros(mla.mla_decode_workspace_bytes(torch.bfloat16, b, h, w.t_max, cfg), dtype=torch.uint8,
+                     device="cuda")
+    out, lse = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale, workspace=ws, config=cfg)
+    torch.cuda.synchronize()
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(b), [0, 31, 64, 127])
+    empty = (lens == 0).nonzero().flatten().tolist()
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+    # the plan left in the workspace is the split rule exactly
+    ref = _plan_model(lens.tolist(), w.t_max, n_chunks, 32)
+    assert ws[:4 * len(ref)].cpu().view(torch.int32).tolist() == ref
