@@ -88,10 +88,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t*
 {
     PlanView v{const_cast<int32_t*>(plan), b};
     const int groups = (h + 3) / 4;
-    const int r = blockIdx.x / groups;
+    // Workgroups go to the 8 XCDs round-robin by id, and the attention kernel
+    // handles the chunks of the batch's eighth x on XCD x: the workgroups of
+    // row r take ids on that XCD, whose L2 may still hold the row's partials.
+    const int b8 = b / 8;
+    int rg = blockIdx.x;
+    if ((int)blockIdx.x < 8 * b8 * groups) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        rg = (x * b8 + j / groups) * groups + j % groups;
+    }
+    const int r = rg / groups;
     // the head is the same for the whole wave: keep it, and every address
     // built on it but the lane's 16 bytes, in scalar registers
-    const int head = __builtin_amdgcn_readfirstlane((blockIdx.x % groups) * 4 + (threadIdx.x >> 6));
+    const int head = __builtin_amdgcn_readfirstlane((rg % groups) * 4 + (threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (head >= h) return;
     const int ns = v.nsplit()[r];
