@@ -96,8 +96,12 @@ class Hip:
 def kernel_source_hash():
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            for line in f:
+                # code only: comments and blank lines do not change the kernel
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

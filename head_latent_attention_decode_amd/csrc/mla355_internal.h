@@ -16,7 +16,8 @@ constexpr int kDv = 128;       // per-head value width (absorb o)
 constexpr int kRowBytesBf16 = kDqk * 2;  // 1152 B: 72 chunks of 16 B
 
 // ---------------------------------------------------------------------------
-// Split plan, built on the device from seqlens by plan_kernel.
+// Split plan, built on the device from seqlens (plan_build.h): by plan_kernel
+// into the workspace, or by each wide attention workgroup into its own LDS.
 // The batch is viewed as one concatenated token sequence (row 0's tokens,
 // then row 1's, ...).  It is cut into n_chunks equal chunks of `chunk`
 // tokens; each chunk (per head group) is one workgroup's work.  A chunk may
