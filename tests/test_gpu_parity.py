@@ -708,3 +708,17 @@ def test_wide_kernel_plan_limits(mla, b, n_chunks):
     # the plan left in the workspace is the split rule exactly
     ref = _plan_model(lens.tolist(), w.t_max, n_chunks, 32)
     assert ws[:4 * len(ref)].cpu().view(torch.int32).tolist() == ref
+
+
+def test_two_head_groups_with_empty_rows(mla):
+    # 256 heads: two groups of 128, each its own attention workgroup per chunk
+    # (both build the same plan); empty rows must be zero across all 256 heads.
+    lens = [0, 700, 33, 0, 1, 4096, 257, 0]
+    w = workloads.make_custom(len(lens), 256, lens, seed=141, device="cuda")
+    for cfg in (None, {"n_chunks": 64}, {"n_chunks": 2560}):
+        out, lse = _run(mla, w, cfg)
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b),
+                     [0, 1, 127, 128, 129, 200, 255])
+        for i, L in enumerate(lens):
+            if L == 0:
+                assert torch.all(out[i] == 0) and torch.all(torch.isneginf(lse[i]))
