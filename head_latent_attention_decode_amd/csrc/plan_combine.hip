@@ -77,7 +77,8 @@ constexpr int kCombineUnroll = 8;     // partial rows in flight per wave
 // usual online log-sum-exp): each round requests its slots' lse values
 // together with their partial rows, so a row with up to kCombineUnroll
 // segments waits on memory once after reading the plan.  Rows with one
-// segment were finished by the decode kernel, rows with none by plan_kernel.
+// segment were finished by the attention kernel, rows with none by whichever
+// kernel built the plan (plan_kernel, or the wide attention kernel itself).
 template <typename OutT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const int32_t* __restrict__ plan,
                                                                   int b, int h,
