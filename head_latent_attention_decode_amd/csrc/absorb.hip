@@ -14,6 +14,7 @@
 // v_mfma_f32_16x16x32_bf16 and the input rows as the B operand, fp32
 // accumulation.  fp32: the vector-ALU kernels below (IEEE fp32 FMAs), one
 // workgroup per (head, block of 16 batch rows).
+#include "append_layout.h"
 #include "bf16_common.h"
 
 namespace mla355 {
@@ -311,8 +312,6 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int M, int H, const __
 // the place of heads: chunk h of every x row times rows h*kAppendKD.. of
 // W_DKV (512 columns, 8 blocks of 64) and of W_KR (64 columns, 1 block), into
 // fp32 partial sums P[m][h][0:576].  One launch covers both weights.
-constexpr int kAppendKD = 256;
-
 __global__ __launch_bounds__(256) void append_proj_kernel(int M, int H, const __bf16* __restrict__ x,
                                                           const __bf16* __restrict__ w_dkv,
                                                           const __bf16* __restrict__ w_kr,
@@ -420,18 +419,6 @@ hipError_t launch_absorb_q(bool bf16, int b, int h, const void* q_nope, const vo
     return hipGetLastError();
 }
 
-// Workspace: fp32 partial sums [b][H][576], then a copy of the b positions.
-size_t append_part_bytes(int b, int d_model)
-{
-    return align_up((size_t)b * (size_t)(d_model / kAppendKD) * kDqk * sizeof(float), 256);
-}
-
-size_t append_workspace_bytes(int b, int d_model)
-{
-    return append_part_bytes(b, d_model) + align_up((size_t)b * sizeof(int32_t), 256);
-}
-
-int append_kd() { return kAppendKD; }
 
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,
                                const void* w_dkv, const void* w_kr, const float* rope_cos,

@@ -4,7 +4,9 @@
 // Validation is pure host code and runs before any HIP call, so every error
 // path can be exercised without a GPU.
 #include "../../include/mla355.h"
+#include "append_layout.h"
 #include "mla355_internal.h"
+#include "variants.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -49,11 +51,11 @@ mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* c
         s->min_chunk = 16;
     } else {
         // <= 16 heads: 16-head workgroups of two token-splitting waves
-        // (memory-bound regime); 17..64 heads: 32x32-MFMA workgroups of 32 or
-        // 64 heads; more: wide-wave workgroups covering 128 heads, so every
-        // latent row is fetched once per head group of 128.
+        // (memory-bound regime); 17..32 heads: 32-head workgroups of 16x16
+        // MFMA tiles; more: wide-wave workgroups (32 heads per wave) of 64 or
+        // 128 heads, so every latent row is fetched once per head group.
         int hpg = h <= 16 ? 16 : h <= 32 ? 32 : h <= 64 ? 64 : 128;
-        int def_variant = h <= 16 ? 1 : h <= 32 ? 1 : h <= 64 ? 3 : 4;
+        int def_variant = h <= 16 ? 1 : h <= 32 ? 1 : h <= 64 ? 6 : 4;
         if (cfg && cfg->heads_per_group != 0) {
             hpg = cfg->heads_per_group;
             def_variant = 1;

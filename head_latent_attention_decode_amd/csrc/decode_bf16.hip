@@ -35,6 +35,10 @@
 //  * Segment end: a row finished inside this chunk writes out (bf16) and lse;
 //    otherwise the normalised fp32 partial and its lse go to the row's slot.
 #include "bf16_common.h"
+#include "variants.h"
+
+#include <array>
+#include <utility>
 
 #include <math.h>
 
@@ -963,116 +967,52 @@ hipError_t launch_variant_fp8(const DecodeParams& p, hipStream_t stream)
     return hipGetLastError();
 }
 
-struct VariantEntry {
-    int heads_per_group;
-    int variant;
-    int tile_tokens;
-    hipError_t (*launch)(const DecodeParams&, hipStream_t);
-    const char* name;        // kernel name as profilers print it
-    const char* paged_name;  // the same for a paged cache; nullptr: not supported
-    hipError_t (*launch_fp8)(const DecodeParams&, hipStream_t);  // fp8 cache; nullptr: none
-    const char* fp8_name;
-    bool plans;  // builds its own split plan in LDS (wide kernels with LDS to spare)
-};
+typedef hipError_t (*LaunchFn)(const DecodeParams&, hipStream_t);
 
-// heads_per_group, variant id, tile tokens, launcher, names, fp8 launcher and name
-const VariantEntry kVariants[] = {
-    {16, 1, 64, &launch_variant<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, false>", nullptr,
-     &launch_variant_fp8<16, 1, 2, 32, 2>, "decode_bf16_kernel<16, 1, 2, 32, 2, true>", false},
-    {16, 2, 32, &launch_variant<16, 1, 1, 32, 2>, "decode_bf16_kernel<16, 1, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr, false},
-    {32, 1, 64, &launch_variant<16, 2, 2, 32, 2>, "decode_bf16_kernel<16, 2, 2, 32, 2, false>", nullptr,
-     nullptr, nullptr, false},
-    {32, 2, 32, &launch_variant<32, 1, 1, 32, 2>, "decode_bf16_kernel<32, 1, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr, false},
-    {64, 1, 64, &launch_variant<16, 4, 1, 64, 2>, "decode_bf16_kernel<16, 4, 1, 64, 2, false>", nullptr,
-     nullptr, nullptr, false},
-    {64, 2, 32, &launch_variant<32, 2, 1, 32, 4>, "decode_bf16_kernel<32, 2, 1, 32, 4, false>", nullptr,
-     nullptr, nullptr, false},
-    {128, 1, 32, &launch_variant<32, 4, 1, 32, 4>, "decode_bf16_kernel<32, 4, 1, 32, 4, false>", nullptr,
-     nullptr, nullptr, false},
-    {128, 2, 32, &launch_variant<16, 8, 1, 32, 2>, "decode_bf16_kernel<16, 8, 1, 32, 2, false>", nullptr,
-     nullptr, nullptr, false},
-    {64, 3, 32, &launch_pair_variant<2, 4>, "decode_pair_kernel<2, 4>", nullptr, nullptr, nullptr, false},
-    // The three-stage ring (pair kernel <2, 3>) is switched off: it took a GPU
-    // memory fault on the edge-length batch (lengths 0..700, 64 heads) whose
-    // cause has not been found; every other variant passes the same tests.
-    {32, 3, 32, &launch_pair_variant<1, 4>, "decode_pair_kernel<1, 4>", nullptr, nullptr, nullptr, false},
-    {128, 3, 32, &launch_decode_wide<4, 3>, "decode_wide_kernel<4, 3, false>", "decode_wide_kernel<4, 3, true>",
-     nullptr, nullptr, true},
-    {128, 4, 32, &launch_decode_wide<4, 2>, "decode_wide_kernel<4, 2, false>", "decode_wide_kernel<4, 2, true>",
-     nullptr, nullptr, true},
-    {128, 5, 32, &launch_decode_wide<4, 4>, "decode_wide_kernel<4, 4, false>", "decode_wide_kernel<4, 4, true>",
-     nullptr, nullptr, false},
-    {64, 5, 32, &launch_decode_wide<2, 3>, "decode_wide_kernel<2, 3, false>", "decode_wide_kernel<2, 3, true>",
-     nullptr, nullptr, true},
-    {64, 6, 32, &launch_decode_wide<2, 2>, "decode_wide_kernel<2, 2, false>", "decode_wide_kernel<2, 2, true>",
-     nullptr, nullptr, true},
-    {32, 4, 32, &launch_decode_wide<1, 3>, "decode_wide_kernel<1, 3, false>", "decode_wide_kernel<1, 3, true>",
-     nullptr, nullptr, true},
-};
-
-const VariantEntry* find_variant(int hpg, int variant)
+// The launcher of variant I (fp8: its fp8-cache form, nullptr if it has none),
+// instantiated from the template arguments the table lists.
+template <int I, bool FP8>
+constexpr LaunchFn variant_launcher()
 {
-    if (variant == 0) variant = 1;
-    for (const auto& v : kVariants)
-        if (v.heads_per_group == hpg && v.variant == variant) return &v;
-    return nullptr;
+    constexpr VariantInfo v = kVariantInfo[I];
+    if constexpr (FP8) {
+        if constexpr (v.family == KernelFamily::Tiled && v.fp8_name != nullptr)
+            return &launch_variant_fp8<v.targs[0], v.targs[1], v.targs[2], v.targs[3], v.targs[4]>;
+        else
+            return nullptr;
+    } else if constexpr (v.family == KernelFamily::Tiled) {
+        return &launch_variant<v.targs[0], v.targs[1], v.targs[2], v.targs[3], v.targs[4]>;
+    } else if constexpr (v.family == KernelFamily::Pair) {
+        return &launch_pair_variant<v.targs[0], v.targs[1]>;
+    } else {
+        return &launch_decode_wide<v.targs[0], v.targs[1]>;
+    }
 }
+
+struct Launchers {
+    LaunchFn launch, launch_fp8;
+};
+
+template <int... I>
+constexpr auto make_launchers(std::integer_sequence<int, I...>)
+{
+    return std::array<Launchers, sizeof...(I)>{Launchers{variant_launcher<I, false>(), variant_launcher<I, true>()}...};
+}
+
+const auto kLaunchers = make_launchers(std::make_integer_sequence<int, kNumVariants>{});
 
 }  // namespace
-
-bool bf16_variant_exists(int heads_per_group, int variant)
-{
-    return find_variant(heads_per_group, variant) != nullptr;
-}
-
-const char* bf16_kernel_name(int heads_per_group, int variant, bool paged)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v == nullptr ? nullptr : (paged ? v->paged_name : v->name);
-}
-
-bool bf16_variant_fp8(int heads_per_group, int variant)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v != nullptr && v->launch_fp8 != nullptr;
-}
-
-const char* fp8_kernel_name(int heads_per_group, int variant)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v == nullptr ? nullptr : v->fp8_name;
-}
-
-bool bf16_variant_plans(int heads_per_group, int variant)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v != nullptr && v->plans;
-}
-
-bool bf16_variant_pages(int heads_per_group, int variant)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v != nullptr && v->paged_name != nullptr;
-}
-
-int bf16_tile_tokens(int heads_per_group, int variant)
-{
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    return v ? v->tile_tokens : 0;
-}
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int variant,
                               hipStream_t stream)
 {
-    const VariantEntry* v = find_variant(heads_per_group, variant);
-    if (!v) return hipErrorInvalidValue;
+    const int i = find_variant_index(heads_per_group, variant);
+    if (i < 0) return hipErrorInvalidValue;
     if (p.cache_scale != nullptr) {
-        if (v->launch_fp8 == nullptr) return hipErrorInvalidValue;
-        return v->launch_fp8(p, stream);
+        if (kLaunchers[i].launch_fp8 == nullptr) return hipErrorInvalidValue;
+        return kLaunchers[i].launch_fp8(p, stream);
     }
-    return v->launch(p, stream);
+    return kLaunchers[i].launch(p, stream);
 }
 
 }  // namespace mla355

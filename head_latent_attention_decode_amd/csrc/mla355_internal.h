@@ -116,13 +116,9 @@ hipError_t launch_plan(const int32_t* seqlens, int b, int h, int t_max, int n_ch
 hipError_t launch_combine(bool bf16, const int32_t* plan, int b, int h, int n_chunks, const float* plse,
                           const void* po, void* out, float* lse, hipStream_t stream);
 
-// bf16 decode variants.  heads_per_group selects the family; variant picks a
-// tiling inside it (0 = default).  Returns hipErrorInvalidValue if absent.
-struct Bf16Variant {
-    int heads_per_group;
-    int variant;
-    int tile_tokens;      // tokens per LDS tile (used for the minimum chunk)
-};
+// bf16 decode variants (table in variants.h, queries in variants.cpp).
+// heads_per_group selects the family; variant picks a tiling inside it
+// (0 = default).  launch_decode_bf16 returns hipErrorInvalidValue if absent.
 bool bf16_variant_exists(int heads_per_group, int variant);
 int bf16_tile_tokens(int heads_per_group, int variant);
 const char* bf16_kernel_name(int heads_per_group, int variant, bool paged);
@@ -155,9 +151,7 @@ hipError_t launch_absorb_o(bool bf16, int b, int h, const void* o, const void* w
 
 // Appending a token's latent row: the hidden dimension must be a multiple of
 // append_kd(); the workspace (partial sums and a copy of the positions) takes
-// append_workspace_bytes(b, d_model).
-int append_kd();
-size_t append_workspace_bytes(int b, int d_model);
+// append_workspace_bytes(b, d_model) (both in append_layout.h).
 // block_table == nullptr: cache [b, t_max, 576]; else cache is the pool
 // [num_blocks, block_size, 576] and t_max = max_blocks * block_size.
 hipError_t launch_cache_append(int b, int d_model, int t_max, int n_pos, const void* x,

@@ -34,29 +34,20 @@ def _rng(seed):
     return np.random.default_rng(seed)
 
 
-def _toy(seed=107, b=1, t=6, h=3, dc=4, dk=5, dr=2, dv=6):
-    """Toy inputs at the glossary check's dimensions.  The upstream projections
-    (hidden -> latent, hidden -> rope key, hidden -> queries) only manufacture
-    inputs; they are not part of the oracle."""
+def _toy(seed, b, t, h, dc, dk, dr, dv):
+    """Inputs at the glossary check's toy widths, drawn directly from one
+    generator: t cached latent rows [c (dc) ; k_R (dr)] per batch row, each
+    head's query split into its no-RoPE part (dk) and RoPE part (dr), and the
+    two up-projections in this library's layouts, W_UK [h, dk, dc] and
+    W_UV [h, dc, dv], scaled by 1/sqrt(contracted width)."""
     g = _rng(seed)
-    hidden = 12
-    x = g.standard_normal((b, t, hidden))
-    x_new = g.standard_normal((b, 1, hidden))
-    w_dkv = g.standard_normal((hidden, dc))
-    w_kr = g.standard_normal((hidden, dr))
-    w_uk = g.standard_normal((h, dk, dc))  # [h, d_k, d_c]
-    w_uv = g.standard_normal((h, dc, dv))  # [h, d_c, d_v]
-    w_qc = g.standard_normal((hidden, h * dk))
-    w_qr = g.standard_normal((hidden, h * dr))
-    latent = x @ w_dkv
-    k_rope = x @ w_kr
-    cache = np.concatenate([latent, k_rope], axis=-1)  # [b, t, dc+dr]
-    q_nope = (x_new @ w_qc).reshape(b, h, dk)
-    q_rope = (x_new @ w_qr).reshape(b, h, dr)
-    seqlens = np.full((b,), t, np.int32)
-    scale = 1.0 / math.sqrt(dk + dr)
+    cache = g.standard_normal((b, t, dc + dr))
+    q_nope = g.standard_normal((b, h, dk))
+    q_rope = g.standard_normal((b, h, dr))
+    w_uk = g.standard_normal((h, dk, dc)) / math.sqrt(dk)
+    w_uv = g.standard_normal((h, dc, dv)) / math.sqrt(dc)
     return dict(cache=cache, q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, w_uv=w_uv,
-                seqlens=seqlens, scale=scale, dc=dc)
+                seqlens=np.full((b,), t, np.int32), scale=1.0 / math.sqrt(dk + dr), dc=dc)
 
 
 def _close(a, b, tol, what):
@@ -75,8 +66,8 @@ def pin_glossary_toy_identities(orc):
     assert 2 * d["hq"] * d["dv"] == gold["printed_per_token_standard_kv_elements"]
     assert d["dc"] + d["dr"] == gold["printed_mla_cached_elements"]
     tol = gold["assert_atol"]
-    for seed in (107, 7, 8):
-        z = _toy(seed=seed, b=d["b"], t=d["t"], h=d["hq"], dc=d["dc"], dk=d["dk"], dr=d["dr"],
+    for seed in (3, 41, 2024):
+        z = _toy(seed, b=d["b"], t=d["t"], h=d["hq"], dc=d["dc"], dk=d["dk"], dr=d["dr"],
                  dv=d["dv"])
         y, lse_x, s_x, _ = orc.decode_unabsorbed(z["q_nope"], z["q_rope"], z["w_uk"], z["w_uv"],
                                                  z["cache"], z["seqlens"], z["scale"],
@@ -252,7 +243,7 @@ def pin_split_merge(orc, seed=19):
 
 def pin_probs_sum_to_one(orc, seed=20):
     """The expanded form's softmax rows sum to 1 and are non-negative."""
-    z = _toy(seed=seed, t=9, h=4)
+    z = _toy(seed, b=1, t=9, h=4, dc=4, dk=5, dr=2, dv=6)
     _, _, _, p = orc.decode_unabsorbed(z["q_nope"], z["q_rope"], z["w_uk"], z["w_uv"], z["cache"],
                                        z["seqlens"], z["scale"], want_scores=True)
     assert np.all(p >= 0.0)

@@ -63,6 +63,53 @@ def test_tiny_fp32_pipeline(mla):
     assert_out(to_np(bufs.lse), lse_x, F32_REL, "lse vs expanded form")
 
 
+@pytest.mark.parametrize("h", [3, 20, 40])
+def test_fp32_partial_head_groups(mla, h):
+    # fp32 kernels with h not a multiple of their 16-head group (the last
+    # group partly empty), edge lengths with NaN tails: every stage against
+    # the oracle, and the step end to end against the expanded form
+    lens = [1, 15, 16, 17, 33, 0, 257]
+    w = workloads.make_custom(len(lens), h, lens, dtype=torch.float32, seed=150 + h, device="cuda",
+                              raw_query=True)
+    qp_gpu = mla.mla_absorb_q(w.q_nope, w.w_uk, w.q_rope)
+    torch.cuda.synchronize()
+    qp_ref = oracle.absorb_q(w.q_nope.cpu(), w.w_uk.cpu(), w.q_rope.cpu())
+    assert_out(to_np(qp_gpu), qp_ref, F32_REL, "q'")
+    qp_in = torch.from_numpy(qp_ref).to(torch.float32).cuda()
+    ref_out, ref_lse = oracle.decode_latent(qp_in.cpu(), w.cache.cpu(), w.seqlens.cpu(), w.scale)
+    fin = np.isfinite(ref_lse)
+    for cfg in (None, {"n_chunks": 8}, {"n_chunks": 64}):
+        out, lse = mla.mla_decode(qp_in, w.cache, w.seqlens, w.scale, config=cfg)
+        torch.cuda.synchronize()
+        assert_out(to_np(out), ref_out, F32_REL, "out %s" % cfg)
+        assert_out(to_np(lse)[fin], ref_lse[fin], F32_REL, "lse %s" % cfg)
+        assert torch.all(out[lens.index(0)] == 0) and torch.all(torch.isneginf(lse[lens.index(0)]))
+    bufs = mla.alloc_step(w.b, w.h, w.t_max, torch.float32)
+    y = mla.mla_step(w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.cache, w.seqlens, w.scale, bufs)
+    torch.cuda.synchronize()
+    y_ref, lse_x = oracle.decode_unabsorbed(w.q_nope.cpu(), w.q_rope.cpu(), w.w_uk.cpu(),
+                                            w.w_uv.cpu(), w.cache.cpu(), w.seqlens.cpu(), w.scale)
+    assert_out(to_np(y), y_ref, F32_REL, "y vs expanded form")
+    assert_out(to_np(bufs.lse)[fin], lse_x[fin], F32_REL, "lse vs expanded form")
+
+
+@pytest.mark.parametrize("b,h", [(40, 3), (40, 16), (17, 20)])
+def test_fp32_absorbs_many_rows(mla, b, h):
+    # fp32 absorbs over more batch rows than one 16-row block (the last block ragged)
+    g = torch.Generator().manual_seed(160 + b + h)
+    q_nope = torch.randn(b, h, 128, generator=g).cuda()
+    q_rope = torch.randn(b, h, 64, generator=g).cuda()
+    w_uk = (torch.randn(h, 128, 512, generator=g) / math.sqrt(128)).cuda()
+    o = torch.randn(b, h, 512, generator=g).cuda()
+    w_uv = (torch.randn(h, 512, 128, generator=g) / math.sqrt(512)).cuda()
+    qp = mla.mla_absorb_q(q_nope, w_uk, q_rope)
+    y = mla.mla_absorb_o(o, w_uv)
+    torch.cuda.synchronize()
+    assert_out(to_np(qp), oracle.absorb_q(q_nope.cpu(), w_uk.cpu(), q_rope.cpu()), F32_REL, "q'")
+    np.testing.assert_array_equal(to_np(qp[..., 512:]), to_np(q_rope))
+    assert_out(to_np(y), oracle.absorb_o(o.cpu(), w_uv.cpu()), F32_REL, "y")
+
+
 # ---------------------------------------------------------------- bf16, small, every output
 
 EDGE_LENS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 0, 700]
@@ -437,6 +484,33 @@ def test_full_long_context_end_to_end(mla):
                                       w.seqlens.cpu(), w.scale)
     ref_y = oracle.absorb_o(ref_out, w.w_uv.cpu()[heads])
     assert_out(to_np(y[:, heads]), ref_y, BF16_OUT_REL, "y")
+
+
+def test_long_context_step_vs_expanded_form(mla):
+    # The long-context step (absorb q -> decode -> absorb o, all on the GPU)
+    # against the oracle's un-absorbed form -- per-head keys and values
+    # expanded from the latent rows, the RoPE score term added, softmax,
+    # weighted sum -- on heads 0, 63 and 127 of all four rows.
+    w = workloads.make(5, device="cuda")
+    heads = [0, 63, 127]
+    bufs = mla.alloc_step(w.b, w.h, w.t_max)
+    y = mla.mla_step(w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.cache, w.seqlens, w.scale, bufs)
+    torch.cuda.synchronize()
+    cache = w.cache.cpu()
+    y_x, lse_x = oracle.decode_unabsorbed(w.q_nope.cpu(), w.q_rope.cpu(), w.w_uk.cpu(), w.w_uv.cpu(),
+                                          cache, w.seqlens.cpu(), w.scale, heads=heads)
+    assert_out(to_np(y[:, heads]), y_x, BF16_OUT_REL, "y vs expanded form")
+    # The step stores the absorbed query in bf16 (the decode's input dtype);
+    # that rounding alone moves the lse by about 1e-3 at this length.  The lse
+    # bound is the decode's own (1e-3) on top of that shift, which the oracle
+    # computes by itself: its latent form fed its own q' rounded to bf16.
+    qp_ref = oracle.absorb_q(w.q_nope.cpu(), w.w_uk.cpu(), w.q_rope.cpu())
+    qp_b = torch.from_numpy(qp_ref[:, heads]).to(torch.bfloat16)
+    _, lse_b = oracle.decode_latent(qp_b, cache, w.seqlens.cpu(), w.scale)
+    shift = float(np.max(np.abs(lse_b - lse_x)))
+    assert_lse(to_np(bufs.lse[:, heads]), lse_x, BF16_LSE_ABS + shift, "lse vs expanded form")
+    # and the decode itself against the latent form fed the GPU's own q'
+    check_decode(bufs.q_prime, w.cache, w.seqlens, w.scale, bufs.out, bufs.lse, range(w.b), heads)
 
 
 # ---- several causal query tokens per row (mla_decode_mtp) ---------------------

@@ -8,10 +8,12 @@ Dimensions follow DeepSeek-V2/V3 as the pages give them: a 512-wide latent
 c_KV plus a 64-wide decoupled RoPE key per cached token (576 per row), a
 128-wide per-head query/value width, and a softmax scale of 1/sqrt(128 + 64).
 
-Recipe (one ``torch.Generator`` per workload, seed = 1000 + config number):
-draw order is sequence lengths (ragged configs only), cache, query side, then
-weights.  Values are fp32 N(0,1) draws, rounded to nearest-even into bf16 where
-the config is bf16; weights are divided by sqrt(fan_in) (128 for W_UK, 512 for
+Recipe (one CPU ``torch.Generator`` per workload, seed = 1000 + config
+number; every tensor is drawn on the CPU and then moved to the requested
+device, so one seed gives the same numbers on every device): draw order is
+sequence lengths (ragged configs only), cache, query side, then weights.
+Values are fp32 N(0,1) draws, rounded to nearest-even into bf16 where the
+config is bf16; weights are divided by sqrt(fan_in) (128 for W_UK, 512 for
 W_UV).  In parity runs every cache row at or past a sequence's length holds
 NaN, so a kernel that reads past the end cannot go unnoticed.
 """
@@ -78,19 +80,23 @@ class Workload:
 
 
 def _randn(shape, gen, device, dtype, divisor=1.0, chunk_rows=None):
-    """fp32 N(0,1) draws (optionally / divisor), rounded to `dtype`."""
+    """fp32 N(0,1) draws from the CPU generator `gen` (optionally / divisor),
+    rounded to `dtype` and placed on `device`.  Large tensors are drawn in
+    consecutive blocks of `chunk_rows` leading rows (the block size is a
+    function of the shape only, so a given shape always gets the same
+    numbers)."""
     if chunk_rows is None or shape[0] <= chunk_rows:
-        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        x = torch.randn(shape, generator=gen, dtype=torch.float32)
         if divisor != 1.0:
             x.div_(divisor)
-        return x.to(dtype)
+        return x.to(dtype).to(device)
     out = torch.empty(shape, device=device, dtype=dtype)
     for i in range(0, shape[0], chunk_rows):
         n = min(chunk_rows, shape[0] - i)
-        x = torch.randn((n,) + tuple(shape[1:]), generator=gen, device=device, dtype=torch.float32)
+        x = torch.randn((n,) + tuple(shape[1:]), generator=gen, dtype=torch.float32)
         if divisor != 1.0:
             x.div_(divisor)
-        out[i:i + n].copy_(x)
+        out[i:i + n].copy_(x.to(dtype))
         del x
     return out
 
@@ -115,7 +121,7 @@ def make_custom(b, h, seqlens, t_max=None, dtype=torch.bfloat16, seed=0, device=
     assert len(seqlens) == b
     if t_max is None:
         t_max = max(1, max(seqlens))
-    gen = torch.Generator(device=device)
+    gen = torch.Generator()
     gen.manual_seed(seed)
     sl = torch.tensor([int(x) for x in seqlens], dtype=torch.int32, device=device)
     chunk = max(1, (1 << 26) // max(1, t_max * D_QK))
@@ -141,15 +147,15 @@ def make(cid: int, device="cpu", poison=True, b=None) -> Workload:
     cfg = CONFIGS[cid]
     seed = 1000 + cid
     bb = cfg.b if b is None else b
-    gen = torch.Generator(device=device)
+    gen = torch.Generator()
     gen.manual_seed(seed)
     if cfg.lengths == "fixed":
         sl = torch.full((bb,), cfg.t_max, dtype=torch.int32, device=device)
     elif cfg.lengths == "list":
         sl = torch.tensor(cfg.length_list[:bb], dtype=torch.int32, device=device)
     else:
-        sl = torch.randint(1, cfg.t_max + 1, (bb,), generator=gen, device=device,
-                           dtype=torch.int64).to(torch.int32)
+        sl = torch.randint(1, cfg.t_max + 1, (bb,), generator=gen,
+                           dtype=torch.int64).to(torch.int32).to(device)
     chunk = max(1, (1 << 26) // (cfg.t_max * D_QK))
     cache = _randn((bb, cfg.t_max, D_QK), gen, device, cfg.dtype, chunk_rows=chunk)
     w = Workload(name=cfg.name, dtype=cfg.dtype, b=bb, h=cfg.h, t_max=cfg.t_max, seqlens=sl,
@@ -169,7 +175,7 @@ def make(cid: int, device="cpu", poison=True, b=None) -> Workload:
 def make_step_weights(b, h, dtype=torch.bfloat16, seed=2002, device="cpu"):
     """q_nope, q_rope, W_UK, W_UV for a full absorb -> decode -> absorb step at
     a decode-only config's shape (same recipe as the end-to-end config)."""
-    gen = torch.Generator(device=device)
+    gen = torch.Generator()
     gen.manual_seed(seed)
     q_nope = _randn((b, h, D_K), gen, device, dtype)
     q_rope = _randn((b, h, D_R), gen, device, dtype)
