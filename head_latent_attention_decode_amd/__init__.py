@@ -61,6 +61,8 @@ _lib.mla_decode.restype = _ci
 _lib.mla_decode.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz, _vp]
 _lib.mla_decode_kernel_name.restype = ctypes.c_char_p
 _lib.mla_decode_kernel_name.argtypes = [_ci, _ci, ctypes.POINTER(MLAConfig)]
+_lib.mla_decode_noalloc.restype = _ci
+_lib.mla_decode_noalloc.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp]
 _lib.mla_decode_ex.restype = _ci
 _lib.mla_decode_ex.argtypes = [_ci, _ci, _ci, _ci, _vp, _vp, _vp, _cf, _vp, _vp, _vp, _sz,
                                ctypes.POINTER(MLAConfig), _vp]
@@ -120,7 +122,10 @@ EXPORTED_SYMBOLS = ("mla_abi_version", "mla_status_string", "mla_absorb_q", "mla
                     "mla_decode_mtp_workspace_bytes", "mla_decode_mtp", "mla_decode_mtp_kernel_name",
                     "mla_decode_mtp_workspace_bytes_ex", "mla_decode_mtp_ex",
                     "mla_cache_append_workspace_bytes", "mla_cache_append", "mla_cache_append_paged",
-                    "mla_decode_mtp_paged_workspace_bytes", "mla_decode_mtp_paged")
+                    "mla_decode_mtp_paged_workspace_bytes", "mla_decode_mtp_paged", "mla_decode_noalloc")
+
+# Size of the library's own device array used by mla_decode_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MLAError(RuntimeError):
@@ -257,6 +262,20 @@ def mla_decode(q_prime, cache, seqlens, softmax_scale, out=None, lse=None, works
     else:
         st = _lib.mla_decode_ex(_dtype_code(dt), b, h, t_max, *args, _cfg(config), _stream(stream))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_noalloc(q_prime, cache, seqlens, softmax_scale, out, lse, stream=None):
+    """mla_decode with the library's own fixed device array as its workspace
+    (the C call allocates nothing).  out [b,h,512] and lse [b,h] fp32 are
+    the caller's; returns (out, lse).  Calls on one GPU share that array."""
+    b, h, _ = q_prime.shape
+    t_max = cache.shape[1]
+    dt = q_prime.dtype
+    args = (_dev(q_prime, "q_prime", (b, h, D_QK), dt), _dev(cache, "cache", (b, t_max, D_QK), dt),
+            _dev(seqlens, "seqlens", (b,), torch.int32), ctypes.c_float(float(softmax_scale)),
+            _dev(out, "out", (b, h, D_C), dt), _dev(lse, "lse", (b, h), torch.float32))
+    _check(_lib.mla_decode_noalloc(_dtype_code(dt), b, h, t_max, *args, _stream(stream)), "mla_decode_noalloc")
     return out, lse
 
 

@@ -363,6 +363,30 @@ mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, con
 const char* mla_decode_fp8_kernel_name(int h, const mla_decode_config_t* config);
 
 /*
+ * mla_decode_noalloc -- mla_decode without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It computes exactly what
+ * mla_decode computes (same kernels, same automatic schedule, bit-identical
+ * results), with the split plan and partial results kept in a fixed device
+ * array of MLA_NOALLOC_SCRATCH_BYTES inside the library.  Each GPU the
+ * library runs on holds its own copy of that array until the process ends;
+ * its address is looked up on the first call on each device.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams or threads) race on it and must be serialised by
+ * the caller.  Arguments as mla_decode without workspace / workspace_bytes.
+ * Errors: those of mla_decode; MLA_ERR_WORKSPACE_TOO_SMALL when the problem
+ * needs more than MLA_NOALLOC_SCRATCH_BYTES of workspace
+ * (mla_decode_workspace_bytes(dtype, b, h, t_max) > the constant; at 128
+ * heads in bf16, batches of up to 250 rows fit); MLA_ERR_HIP if the array's
+ * device address cannot be found.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status_t mla_decode_noalloc(mla_dtype_t dtype, int b, int h, int t_max, const void* q_prime,
+                                const void* cache, const int32_t* seqlens, float softmax_scale,
+                                void* out, float* lse, void* stream);
+
+/*
  * mla_absorb_o -- output absorption.
  *   y[b,h,:] = o[b,h,:] . W_UV[h]   (contracts d_c = 512)
  * Glossary, section on why decode absorbs: sum_t p_t (c_t W^UV_h) equals
