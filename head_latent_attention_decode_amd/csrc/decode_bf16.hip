@@ -984,6 +984,8 @@ constexpr LaunchFn variant_launcher()
         return &launch_variant<v.targs[0], v.targs[1], v.targs[2], v.targs[3], v.targs[4]>;
     } else if constexpr (v.family == KernelFamily::Pair) {
         return &launch_pair_variant<v.targs[0], v.targs[1]>;
+    } else if constexpr (v.family == KernelFamily::Split) {
+        return &launch_decode_colsplit;
     } else {
         return &launch_decode_wide<v.targs[0], v.targs[1]>;
     }

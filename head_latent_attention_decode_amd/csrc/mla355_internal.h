@@ -139,6 +139,9 @@ hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
 template <int NW, int STAGES>
 hipError_t launch_decode_wide_causal(const DecodeParams& p, hipStream_t stream);
 
+// Column-split, software-pipelined bf16 kernel for groups of 128 heads.
+hipError_t launch_decode_colsplit(const DecodeParams& p, hipStream_t stream);
+
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(long long n_rows, const void* x, void* codes, float* scale,

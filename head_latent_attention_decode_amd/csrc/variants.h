@@ -12,6 +12,7 @@ enum class KernelFamily {
     Tiled,  // decode_bf16_kernel<WH, HS, TS, NT, STAGES, FP8>
     Pair,   // decode_pair_kernel<P, STAGES>
     Wide,   // decode_wide_kernel<NW, STAGES, PAGED>
+    Split,  // decode_colsplit_kernel<PAGED>: 128 heads, weighted sum split by columns
 };
 
 struct VariantInfo {
@@ -60,6 +61,8 @@ inline constexpr VariantInfo kVariantInfo[] = {
      nullptr, true},
     {32, 4, 32, KernelFamily::Wide, {1, 3}, "decode_wide_kernel<1, 3, false>", "decode_wide_kernel<1, 3, true>",
      nullptr, true},
+    {128, 6, 32, KernelFamily::Split, {}, "decode_colsplit_kernel<false>", "decode_colsplit_kernel<true>", nullptr,
+     true},
 };
 inline constexpr int kNumVariants = (int)(sizeof(kVariantInfo) / sizeof(kVariantInfo[0]));
 

@@ -310,7 +310,8 @@ void schedules()
                           {64, 0, 0},   {64, 64, 2},  {128, 0, 0},  {128, 128, 2}, {128, 64, 0}, {128, 16, 0},
                           {40, 16, 0},  {64, 64, 3},  {32, 32, 3},  {100, 0, 0},  {16, 16, 1},  {128, 128, 3},
                           {128, 128, 4}, {128, 128, 5}, {100, 128, 3}, {64, 64, 5}, {64, 64, 6},  {32, 32, 4},
-                          {20, 32, 4},  {48, 0, 0},   {33, 0, 0},   {256, 0, 0}};
+                          {20, 32, 4},  {48, 0, 0},   {33, 0, 0},   {256, 0, 0},  {128, 128, 6},
+                          {100, 128, 6}, {256, 128, 6}};
     for (const V& v : variants)
         for (int n : {0, 8, 64, 256, 2560}) {
             mla_decode_config_t c = cfg_of(n, v.hpg, v.variant);

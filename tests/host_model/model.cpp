@@ -312,6 +312,10 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int va
         return hipSuccess;
     case KernelFamily::Wide:
         return wide_launch(p, v->targs[0], v->targs[1], [&](const Shape& s) { walk_split(p, s); });
+    case KernelFamily::Split:
+        if (p.plan_in_kernel && (p.b > kPlanLdsRows || p.n_chunks > kPlanLdsChunks)) return hipErrorInvalidValue;
+        walk_split(p, Shape{128, 32, true, true, 2, row_bytes});
+        return hipSuccess;
     }
     return hipErrorInvalidValue;
 }

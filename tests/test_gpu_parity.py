@@ -132,6 +132,9 @@ BF16_CASES = [
     (100, {"heads_per_group": 128, "variant": 3}), (64, {"heads_per_group": 64, "variant": 5}),
     (64, {"heads_per_group": 64, "variant": 6}), (32, {"heads_per_group": 32, "variant": 4}),
     (20, {"heads_per_group": 32, "variant": 4}),
+    # column-split, pipelined kernel (128 heads per workgroup)
+    (128, {"heads_per_group": 128, "variant": 6}), (100, {"heads_per_group": 128, "variant": 6}),
+    (3, {"heads_per_group": 128, "variant": 6}),
 ]
 
 
@@ -158,6 +161,7 @@ RESCALE_CASES = [
     (128, None), (128, {"heads_per_group": 128, "variant": 3}), (128, {"heads_per_group": 128, "variant": 5}),
     (64, {"heads_per_group": 64, "variant": 6}), (64, {"heads_per_group": 64, "variant": 2}),
     (32, {"heads_per_group": 32, "variant": 4}), (128, {"heads_per_group": 16}),
+    (128, {"heads_per_group": 128, "variant": 6}), (100, {"heads_per_group": 128, "variant": 6}),
 ]
 
 
@@ -309,6 +313,7 @@ PAGED_CASES = [
     (128, 64, None), (128, 32, None), (128, 256, None), (100, 64, None), (64, 64, None),
     (16, 64, None), (20, 32, None),
     (128, 64, {"heads_per_group": 128, "variant": 3}), (64, 128, {"heads_per_group": 64, "variant": 5}),
+    (128, 64, {"heads_per_group": 128, "variant": 6}), (100, 32, {"heads_per_group": 128, "variant": 6}),
 ]
 
 
@@ -438,6 +443,18 @@ def _full(mla, cid, rows):
 
 def test_full_dsv3_decode_b64_h128_T4096(mla):
     _full(mla, 2, [0, 17, 42, 63])
+
+
+def test_full_dsv3_decode_colsplit_kernel(mla):
+    # the 128-head configuration through the column-split kernel explicitly,
+    # sampled rows, run-to-run bit equality
+    w = workloads.make(2, device="cuda")
+    cfg = {"heads_per_group": 128, "variant": 6}
+    out, lse = _run(mla, w, cfg)
+    out2, lse2 = _run(mla, w, cfg)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert torch.isfinite(out).all()
+    check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, [0, 17, 42, 63])
 
 
 def test_full_dsv3_decode_paged_bs64(mla):
