@@ -29,6 +29,8 @@ import hashlib
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -118,6 +120,62 @@ def load_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def sample_clock(torch, run):
+    """Engine clock (MHz) read from the host through amdsmi while `run()`
+    keeps the GPU busy: median, min and max of the samples, or None where
+    the query is not available."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                samples.append(float(torch.cuda.clock_rate(0)))
+            except Exception:
+                return
+            time.sleep(0.0005)
+
+    t = threading.Thread(target=poll, daemon=True)
+    t.start()
+    run()
+    torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    samples = [x for x in samples if x > 0]
+    if not samples:
+        return None
+    return {"median": statistics.median(samples), "min": min(samples), "max": max(samples),
+            "samples": len(samples), "source": "amdsmi, sampled during 400 back-to-back steps"}
+
+
+def copy_bandwidth(torch, dev, hip, stream, nbytes=1 << 30):
+    """Device-to-device copy of 1 GiB (context for the HBM figures): bytes
+    read plus bytes written over the best of three copies, GB/s."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(3):
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        dst.copy_(src)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        t = hip.elapsed_ms(e0, e1)
+        best = t if best is None else min(best, t)
+    del src, dst
+    return round(2 * nbytes / (best * 1e-3) / 1e9, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None, q_len=1):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole batch rows, all heads (and query tokens), absorb -> latent
@@ -156,7 +214,7 @@ def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None, q_
     dt, fl = run(rows)
     toks = "" if q_len == 1 else " x %d query tokens" % q_len
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d batch rows%s, all %d heads, %d cached tokens each: fp64 absorb_q -> "
                       "latent-form decode -> absorb_o, %.1f s" % (n, w.b, toks, w.h, lens[0], dt)}
 
@@ -505,17 +563,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [hip.elapsed_ms(e[0], e[3]) for e in ev]
-    for i in range(K):
+    # the kernel pass: at least 50 launches for the median and minimum
+    KK = max(K, 50)
+    ev += [[hip.event() for _ in range(4)] for _ in range(KK - K)]
+    for i in range(KK):
         if flush is not None:
             flush.sum()
         hip.record(ev[i][0], stream)
         step(i)
         hip.record(ev[i][3], stream)
     torch.cuda.synchronize()
-    kern_ms = [hip.elapsed_ms(e[1], e[2]) for e in ev]
-    step_instr_ms = sum(hip.elapsed_ms(e[0], e[3]) for e in ev) / K
+    kern_ms = [hip.elapsed_ms(e[1], e[2]) for e in ev[:KK]]
+    step_instr_ms = sum(hip.elapsed_ms(e[0], e[3]) for e in ev[:KK]) / KK
 
-    # back-to-back steps (no eviction): context only
+    # back-to-back steps (no eviction): context only; the engine clock is
+    # sampled from the host (amdsmi) while a longer run of them executes
     torch.cuda.synchronize()
     b0, b1 = hip.event(), hip.event()
     hip.record(b0, stream)
@@ -524,6 +586,8 @@ def main():
     hip.record(b1, stream)
     torch.cuda.synchronize()
     b2b_ms = hip.elapsed_ms(b0, b1) / K
+    clock = sample_clock(torch, lambda: [step() for _ in range(400)])
+    copy_gbs = copy_bandwidth(torch, dev, hip, stream)
 
     cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize, q_len=q_len)
     if args.fp8:
@@ -534,7 +598,7 @@ def main():
     step_bytes = sum(bb for _, bb in cnt.values())
     dec_flop, dec_bytes = cnt["decode"]
     ms = sum(step_ms) / K
-    kms = sum(kern_ms) / K
+    kms = sum(kern_ms) / len(kern_ms)
     value = step_flop / (ms * 1e-3) / 1e12
     k_gbs = dec_bytes / (kms * 1e-3) / 1e9
     k_tfl = dec_flop / (kms * 1e-3) / 1e12
@@ -576,6 +640,12 @@ def main():
         "step_bytes": step_bytes,
         "ms_per_step_back_to_back": round(b2b_ms, 5),
         "ms_per_step_kernel_events": round(step_instr_ms, 5),
+        "step_us": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(step_ms) * 1e3, 2),
+                    "min": round(min(step_ms) * 1e3, 2), "runs": K},
+        "kernel_us": {"mean": round(kms * 1e3, 2), "median": round(statistics.median(kern_ms) * 1e3, 2),
+                      "min": round(min(kern_ms) * 1e3, 2), "runs": len(kern_ms)},
+        "engine_clock_mhz": clock,
+        "copy_1gib_gbps": copy_gbs,
         "roofline": {"kernel": (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
                                 else mla.mla_decode_fp8_kernel_name(w.h, sched or None) if args.fp8
                                 else mla.mla_decode_mtp_kernel_name(q_len, w.h) if mtp is not None

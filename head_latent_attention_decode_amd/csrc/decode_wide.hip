@@ -209,7 +209,16 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         const bool final_out = pl_nsplit(r) == 1;
         const int slot = pl_base(r) + split_j;
         const unsigned char* seg_base = cg + ((size_t)r * p.t_max + seg_a) * kRowBytesBf16;
-        const int n_tiles = (seg_len + T::N - 1) / T::N;
+        int n_tiles = (seg_len + T::N - 1) / T::N;
+        if constexpr (CAUSAL) {
+            // Tiles past the causal limit of every query row of this
+            // workgroup hold nothing any of its rows may see: the segment
+            // stops at the last tile the latest row can reach.
+            const int last_row = min(hg * T::HG + T::HG, p.h) - 1;
+            const int L = PAGED ? min(max(seqlen_of(r), 0), p.t_max) : row_hi - row_lo;
+            const int lim_max = L - p.q_len + 1 + last_row / p.heads_per_token - seg_a;
+            n_tiles = max(0, min(n_tiles, (lim_max + T::N - 1) / T::N));
+        }
 
         // Global address of the first row of `tile`.  Paged: tiles are issued
         // once each, in increasing order, so the block-table position of the

@@ -539,6 +539,10 @@ MTP_CASES = [
     (4, 8, [129, 32, 31, 5]),            # 32 rows
     (2, 100, [513, 96]),                 # 200 rows, the last group padded
     (8, 16, [300, 40, 8]),               # 128 rows, a row of exactly q_len
+    (160, 8, [700, 300, 160]),           # prefill-sized: 1280 query rows per batch row, tiles
+                                         # past a query group's causal limits skipped
+    (96, 16, [2000, 97, 96]),            # 1536 query rows; most chunks of the long row hold
+                                         # tokens only the later query groups see
 ]
 
 
