@@ -43,10 +43,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 D_C, D_R, D_QK, D_K, D_V = 512, 64, 576, 128, 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-# sources of the dominant (split-KV attention) kernel: the traffic figures in
-# TRAFFIC_FILE are only valid while these are unchanged
-KERNEL_SRCS = [os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", f)
-               for f in ("decode_wide.hip", "bf16_common.h", "mla355_internal.h", "plan_build.h")]
+# sources of the split-KV attention kernels: a traffic figure in TRAFFIC_FILE
+# is only valid while the common files and its kernel's own file are unchanged
+_CSRC = os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc")
+KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("bf16_common.h", "mla355_internal.h", "plan_build.h")]
+FAMILY_SRCS = {"decode_wide_kernel": "decode_wide.hip", "decode_wide_causal_kernel": "decode_wide.hip",
+               "decode_bf16_kernel": "decode_bf16.hip", "decode_pair_kernel": "decode_bf16.hip",
+               "decode_colsplit_kernel": "decode_colsplit.hip", "decode_f32_kernel": "decode_f32.hip"}
 
 
 def log(*a):
@@ -95,9 +98,14 @@ class Hip:
         return float(ms.value)
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel=None):
+    """Hash of the code lines of the common kernel sources, plus the file of
+    `kernel` (a name such as "decode_wide_kernel<4, 2, false>") if given."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    files = list(KERNEL_SRCS)
+    if kernel is not None:
+        files.append(os.path.join(_CSRC, FAMILY_SRCS[kernel.split("<")[0].strip()]))
+    for path in files:
         with open(path) as f:
             for line in f:
                 # code only: comments and blank lines do not change the kernel
@@ -107,15 +115,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM bytes per split-kernel launch from committed rocprofv3 --pmc runs,
-    valid only while the kernel source is unchanged since the counters were taken."""
+def load_traffic(workload, kernel, path=None):
+    """HBM bytes per launch of `kernel` on `workload` from committed rocprofv3
+    --pmc runs (TRAFFIC_FILE maps workload names to entries), valid only while
+    the kernel's sources are unchanged since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+        with open(path or TRAFFIC_FILE) as f:
+            t = json.load(f).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_hash() or t.get("workload") != workload:
+    if not isinstance(t, dict) or t.get("kernel") != kernel:
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -221,11 +232,11 @@ def cpu_baseline(w, q_nope, q_rope, w_uk, w_uv, target_s=12.0, max_rows=None, q_
 
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o trace -- "
-             "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-context{cfg}",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o fetch -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-context{cfg}",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o write -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-context{cfg}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o cfetch -- "
               "python3 bench.py --calibrate-copy 256",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o cwrite -- "
@@ -233,13 +244,19 @@ PROFILE_CMDS = {
 }
 
 
-def summarize_profiles(dirs, workload="dsv3_decode_b64_h128_T4096"):
-    """Turn the five rocprofv3 runs of PROFILE_CMDS (output directories in that
-    order) into the committed summaries: profiles/<kernel>_<workload>.md and
-    the traffic figures bench.py reports (profiles/decode_traffic.json).
-    Pure file processing, no GPU."""
+def summarize_profiles(dirs, cid=2, out_dir=None):
+    """Turn the five rocprofv3 runs of PROFILE_CMDS for configuration `cid`
+    (output directories in that order) into the committed summaries:
+    profiles/<kernel>_<workload>.md and the workload's entry of the traffic
+    figures bench.py reports (profiles/decode_traffic.json).  Pure file
+    processing, no GPU.  out_dir replaces profiles/ (tests)."""
     import csv
     import glob
+    import workloads
+    cfg = workloads.CONFIGS[cid]
+    workload = cfg.name
+    lens = workloads.lengths(cid)
+    cfg_arg = "" if cid == 2 else " --config %d" % cid
 
     def rows(d, suffix):
         files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
@@ -275,22 +292,26 @@ def summarize_profiles(dirs, workload="dsv3_decode_b64_h128_T4096"):
     short = re.search(r"decode_\w+(<[^>]*>)?", dname).group(0)
     family = short.split("<")[0]
     hbm = int(round((fetch[dname] * fs + write[dname] * ws_) * 1024))
-    w = workloads_counts(workload)
+    w = work_counts(cfg.b, cfg.h, lens, elt=cfg.dtype.itemsize)["decode"][1]
     traffic = {
-        "kernel": short, "kernel_source_sha": kernel_source_hash(), "workload": workload,
+        "kernel": short, "kernel_source_sha": kernel_source_hash(short), "workload": workload,
         "hbm_bytes_per_launch": hbm, "fetch_kib_per_launch": round(fetch[dname], 1),
         "write_kib_per_launch": round(write[dname], 1), "fetch_scale": round(fs, 4),
         "write_scale": round(ws_, 4),
         "calibration": "plain 256 MiB device copy (bench.py --calibrate-copy 256): FETCH_SIZE "
                        "%.1f KiB, WRITE_SIZE %.1f KiB per copy" % (cf, cw)}
-    lines = ["# %s on %s (bf16, b=64, h=128, 4096 cached tokens)" % (short, workload), "",
+    toks = ("%d cached tokens" % lens[0] if len(set(lens)) == 1 else
+            "%d to %d cached tokens, %d in all" % (min(lens), max(lens), sum(lens)))
+    lines = ["# %s on %s (%s, b=%d, h=%d, %s)" % (short, workload, str(cfg.dtype).split(".")[-1], cfg.b,
+                                                  cfg.h, toks), "",
              "MI355X (gfx950), ROCm 7.2, one GPU.  Commands, run from the repository root with",
              "`export TMPDIR=/tmp` (DIR: any output directory), then this summary:", "", "```"]
-    lines += [PROFILE_CMDS[k] for k in ("trace", "fetch", "write", "cfetch", "cwrite")]
-    lines += ["python3 bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR CFETCH_DIR CWRITE_DIR",
+    lines += [PROFILE_CMDS[k].replace("{cfg}", cfg_arg) for k in ("trace", "fetch", "write", "cfetch", "cwrite")]
+    lines += ["python3 bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR CFETCH_DIR CWRITE_DIR%s" % cfg_arg,
               "```", "", "## Kernel trace (`*_kernel_stats.csv`), durations in microseconds", "",
               "Calls include warm-up steps; `reduce_kernel` is the cache-evicting read of a",
-              "512 MiB buffer between steps (outside the timed region).", "",
+              "512 MiB buffer between steps and `__amd_rocclr_fillBufferAligned` the zeroing",
+              "that reduction does first (both outside the timed region).", "",
               "| kernel | calls | avg | min | max | % |", "|---|---|---|---|---|---|"]
     for r in stats:
         nm = r["Name"]
@@ -311,24 +332,25 @@ def summarize_profiles(dirs, workload="dsv3_decode_b64_h128_T4096"):
     lines += ["", "Algorithmic bytes of one attention launch: %.1f MB (latent cache, queries," % (w / 1e6),
               "outputs and lse).  Measured %.1f MB; the difference is mostly the split-KV" % (hbm / 1e6),
               "partials (written here, read back by the combine kernel)."]
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", "%s_%s.md" % (family, workload))
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    traffic_file = os.path.join(out_dir, os.path.basename(TRAFFIC_FILE))
+    os.makedirs(out_dir, exist_ok=True)
+    md = os.path.join(out_dir, "%s_%s.md" % (family, workload))
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(traffic, f, indent=1)
+    try:
+        with open(traffic_file) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    if not isinstance(table, dict) or "kernel" in table:
+        table = {}
+    table[workload] = traffic
+    with open(traffic_file, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
         f.write("\n")
     print(md)
-    print(TRAFFIC_FILE)
-
-
-def workloads_counts(workload):
-    """Algorithmic bytes of one attention launch of a named workload."""
-    import workloads
-    for cfg in workloads.CONFIGS.values():
-        if cfg.name == workload and cfg.lengths == "fixed":
-            return work_counts(cfg.b, cfg.h, [cfg.t_max] * cfg.b)["decode"][1]
-    raise SystemExit("no fixed-length workload named %s" % workload)
+    print(traffic_file)
 
 
 def bench_append(args, torch, mla, workloads, dev):
@@ -395,6 +417,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload configuration (1..5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements (back-to-back steps, engine clock, device "
+                         "copy), so that a profiled run holds only evicted-cache launches")
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--hpg", type=int, default=0, help="heads per workgroup (0 = auto)")
     ap.add_argument("--variant", type=int, default=0)
@@ -421,10 +446,10 @@ def main():
                          "and exit (no GPU needed)")
     args = ap.parse_args()
     if args.print_source_hash:
-        print(kernel_source_hash())
+        print(kernel_source_hash("decode_wide_kernel"))
         return
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.config)
         return
 
     if args.gpus != 1:
@@ -578,16 +603,18 @@ def main():
 
     # back-to-back steps (no eviction): context only; the engine clock is
     # sampled from the host (amdsmi) while a longer run of them executes
-    torch.cuda.synchronize()
-    b0, b1 = hip.event(), hip.event()
-    hip.record(b0, stream)
-    for _ in range(K):
-        step()
-    hip.record(b1, stream)
-    torch.cuda.synchronize()
-    b2b_ms = hip.elapsed_ms(b0, b1) / K
-    clock = sample_clock(torch, lambda: [step() for _ in range(400)])
-    copy_gbs = copy_bandwidth(torch, dev, hip, stream)
+    b2b_ms = clock = copy_gbs = None
+    if not args.no_context:
+        torch.cuda.synchronize()
+        b0, b1 = hip.event(), hip.event()
+        hip.record(b0, stream)
+        for _ in range(K):
+            step()
+        hip.record(b1, stream)
+        torch.cuda.synchronize()
+        b2b_ms = hip.elapsed_ms(b0, b1) / K
+        clock = sample_clock(torch, lambda: [step() for _ in range(400)])
+        copy_gbs = copy_bandwidth(torch, dev, hip, stream)
 
     cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize, q_len=q_len)
     if args.fp8:
@@ -602,13 +629,17 @@ def main():
     value = step_flop / (ms * 1e-3) / 1e12
     k_gbs = dec_bytes / (kms * 1e-3) / 1e9
     k_tfl = dec_flop / (kms * 1e-3) / 1e12
-    traffic = None if (args.paged or args.fp8 or mtp is not None) else load_traffic(cfg.name)
+    kname = (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
+             else mla.mla_decode_fp8_kernel_name(w.h, sched or None) if args.fp8
+             else mla.mla_decode_mtp_kernel_name(q_len, w.h) if mtp is not None
+             else mla.mla_decode_kernel_name(w.dtype, w.h, sched or None))
+    traffic = None if (args.paged or args.fp8 or mtp is not None) else load_traffic(cfg.name, kname)
     # the roof the attention kernel meets first: HBM bytes or MFMA FLOPs
     mfma_bound = dec_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12) > dec_bytes / (HBM_PEAK_GBS * 1e9)
     log("step: mean %.2f us (min %.2f, max %.2f); split-KV kernel mean %.2f us (min %.2f); "
         "back-to-back step %.2f us; wall %.3f s for %d steps" %
         (ms * 1e3, min(step_ms) * 1e3, max(step_ms) * 1e3, kms * 1e3, min(kern_ms) * 1e3,
-         b2b_ms * 1e3, wall, K))
+         (b2b_ms or 0.0) * 1e3, wall, K))
     log("split-KV kernel: %.1f GB/s (%.1f%% of HBM), %.1f TFLOP/s (%.1f%% of bf16 MFMA)" %
         (k_gbs, 100 * k_gbs / HBM_PEAK_GBS, k_tfl, 100 * k_tfl / MFMA_BF16_PEAK_TFLOPS))
 
@@ -638,7 +669,7 @@ def main():
         "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_flop": step_flop,
         "step_bytes": step_bytes,
-        "ms_per_step_back_to_back": round(b2b_ms, 5),
+        "ms_per_step_back_to_back": None if b2b_ms is None else round(b2b_ms, 5),
         "ms_per_step_kernel_events": round(step_instr_ms, 5),
         "step_us": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(step_ms) * 1e3, 2),
                     "min": round(min(step_ms) * 1e3, 2), "runs": K},
@@ -646,10 +677,7 @@ def main():
                       "min": round(min(kern_ms) * 1e3, 2), "runs": len(kern_ms)},
         "engine_clock_mhz": clock,
         "copy_1gib_gbps": copy_gbs,
-        "roofline": {"kernel": (mla.mla_decode_paged_kernel_name(w.h, sched or None) if args.paged
-                                else mla.mla_decode_fp8_kernel_name(w.h, sched or None) if args.fp8
-                                else mla.mla_decode_mtp_kernel_name(q_len, w.h) if mtp is not None
-                                else mla.mla_decode_kernel_name(w.dtype, w.h, sched or None)),
+        "roofline": {"kernel": kname,
                      "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(kms * 1e3, 2),

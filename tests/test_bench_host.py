@@ -52,3 +52,56 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
         monkeypatch.setattr(bench, "KERNEL_SRCS", [str(path)])
         hashes.append(bench.kernel_source_hash())
     assert hashes[0] == hashes[1] != hashes[2]
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_profile_summary_per_workload(tmp_path):
+    """Five fake rocprofv3 output directories for the few-heads workload: the
+    summary lands under its own name, its traffic entry sits beside the other
+    workloads' entries, and the bench's lookup finds it only for the kernel
+    it was taken from."""
+    kern = "void mla355::(anonymous namespace)::decode_bf16_kernel<16, 1, 2, 32, 2, false>(mla355::DecodeParams)"
+    copy = "void at::native::copy_kernel"
+    d = {k: tmp_path / k for k in ("trace", "fetch", "write", "cfetch", "cwrite")}
+    _write_csv(str(d["trace"] / "x" / "trace_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [[kern, 13, 2.8e6, 219000.0, 80.0, 210000.0, 230000.0]])
+    # two dispatches, each counted over two hardware instances
+    cnt = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write_csv(str(d["fetch"] / "x" / "fetch_counter_collection.csv"), cnt,
+               [[1, kern, "FETCH_SIZE", 50000.0], [1, kern, "FETCH_SIZE", 50000.0],
+                [2, kern, "FETCH_SIZE", 60000.0], [2, kern, "FETCH_SIZE", 40000.0]])
+    _write_csv(str(d["write"] / "x" / "write_counter_collection.csv"), cnt,
+               [[1, kern, "WRITE_SIZE", 1000.0], [2, kern, "WRITE_SIZE", 1000.0]])
+    _write_csv(str(d["cfetch"] / "x" / "cfetch_counter_collection.csv"), cnt,
+               [[7, copy, "FETCH_SIZE", 131072.0]])
+    _write_csv(str(d["cwrite"] / "x" / "cwrite_counter_collection.csv"), cnt,
+               [[7, copy, "WRITE_SIZE", 262144.0]])
+    out = tmp_path / "profiles"
+    out.mkdir()
+    # an entry of another workload already there is kept
+    (out / "decode_traffic.json").write_text('{"other_workload": {"kernel": "k"}}\n')
+    bench.summarize_profiles([str(d[k]) for k in ("trace", "fetch", "write", "cfetch", "cwrite")],
+                             cid=3, out_dir=str(out))
+    md = (out / "decode_bf16_kernel_few_heads_b128_h16_T8192.md").read_text()
+    assert "--config 3" in md and "219.0" in md
+    import json
+    table = json.loads((out / "decode_traffic.json").read_text())
+    assert set(table) == {"other_workload", "few_heads_b128_h16_T8192"}
+    e = table["few_heads_b128_h16_T8192"]
+    # FETCH_SIZE: 100000 KiB per dispatch x (256 MiB / 131072 KiB) = 2; WRITE_SIZE x 1
+    assert e["hbm_bytes_per_launch"] == (100000 * 2 + 1000) * 1024
+    name = "decode_bf16_kernel<16, 1, 2, 32, 2, false>"
+    assert e["kernel"] == name
+    path = str(out / "decode_traffic.json")
+    assert bench.load_traffic("few_heads_b128_h16_T8192", name, path) == e["hbm_bytes_per_launch"]
+    assert bench.load_traffic("few_heads_b128_h16_T8192", "decode_wide_kernel<4, 2, false>", path) is None
+    assert bench.load_traffic("dsv3_decode_b64_h128_T4096", name, path) is None

@@ -140,6 +140,25 @@ def make_custom(b, h, seqlens, t_max=None, dtype=torch.bfloat16, seed=0, device=
     return w
 
 
+def _draw_lengths(cfg, gen, bb):
+    """The sequence lengths of a configuration: the first draw from its
+    generator (ragged configs only)."""
+    if cfg.lengths == "fixed":
+        return torch.full((bb,), cfg.t_max, dtype=torch.int32)
+    if cfg.lengths == "list":
+        return torch.tensor(cfg.length_list[:bb], dtype=torch.int32)
+    return torch.randint(1, cfg.t_max + 1, (bb,), generator=gen, dtype=torch.int64).to(torch.int32)
+
+
+def lengths(cid: int) -> list:
+    """Sequence lengths of configuration `cid` exactly as make() draws them,
+    without building the cache."""
+    cfg = CONFIGS[cid]
+    gen = torch.Generator()
+    gen.manual_seed(1000 + cid)
+    return [int(x) for x in _draw_lengths(cfg, gen, cfg.b).tolist()]
+
+
 def make(cid: int, device="cpu", poison=True, b=None) -> Workload:
     """Build configuration `cid` (1..5).  `b` optionally truncates the batch
     (the first b rows of the same draw order are not reproduced; it is a
@@ -149,13 +168,7 @@ def make(cid: int, device="cpu", poison=True, b=None) -> Workload:
     bb = cfg.b if b is None else b
     gen = torch.Generator()
     gen.manual_seed(seed)
-    if cfg.lengths == "fixed":
-        sl = torch.full((bb,), cfg.t_max, dtype=torch.int32, device=device)
-    elif cfg.lengths == "list":
-        sl = torch.tensor(cfg.length_list[:bb], dtype=torch.int32, device=device)
-    else:
-        sl = torch.randint(1, cfg.t_max + 1, (bb,), generator=gen,
-                           dtype=torch.int64).to(torch.int32).to(device)
+    sl = _draw_lengths(cfg, gen, bb).to(device)
     chunk = max(1, (1 << 26) // (cfg.t_max * D_QK))
     cache = _randn((bb, cfg.t_max, D_QK), gen, device, cfg.dtype, chunk_rows=chunk)
     w = Workload(name=cfg.name, dtype=cfg.dtype, b=bb, h=cfg.h, t_max=cfg.t_max, seqlens=sl,
