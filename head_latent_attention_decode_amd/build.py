@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla355.so")
-SOURCES = ["api.cpp", "variants.cpp", "plan_combine.hip", "decode_bf16.hip", "decode_wide.hip", "decode_colsplit.hip", "decode_f32.hip", "absorb.hip",
+SOURCES = ["api.cpp", "variants.cpp", "plan_combine.hip", "decode_bf16.hip", "decode_wide.hip", "decode_colsplit.hip", "decode_wide_fp8.hip", "decode_f32.hip", "absorb.hip",
            "quantize.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -102,20 +102,21 @@ bool paged_dims_ok(int b, int h, int num_blocks, int block_size, int max_blocks)
     return true;
 }
 
-// Schedule for an fp8 cache: the 16-head two-wave kernel is the one with an
-// fp8 form (the regime where halving the bytes pays is few heads per group).
+// Schedule for an fp8 cache.  Up to 64 heads: the 16-head two-wave kernel
+// (exact bf16 queries, bf16 MFMAs).  More: the 128-head wide kernel, which
+// also quantises the queries and scores on FP8 MFMAs.
 mla_status_t choose_fp8_schedule(int h, const mla_decode_config_t* cfg, Schedule* s)
 {
     mla_decode_config_t c{};
     if (cfg) c = *cfg;
-    if (c.heads_per_group == 0) c.heads_per_group = 16;
-    if (c.variant == 0) c.variant = 1;
+    if (c.heads_per_group == 0) c.heads_per_group = h <= 64 ? 16 : 128;
+    if (c.variant == 0) c.variant = c.heads_per_group == 128 ? 4 : 1;
     const mla_status_t st = choose_schedule(MLA_DTYPE_BF16, h, &c, s);
     if (st != MLA_OK) return st;
     if (!bf16_variant_fp8(s->hpg, s->variant)) return MLA_ERR_UNSUPPORTED;
-    // the fp8 form needs 77 KB of LDS: two workgroups fit on a CU, so the
-    // automatic grid is twice as large
-    if (c.n_chunks == 0) s->n_chunks = round_down8(2 * kCUs / s->n_hg);
+    // the 16-head fp8 form needs 77 KB of LDS: two workgroups fit on a CU, so
+    // the automatic grid is twice as large
+    if (c.n_chunks == 0 && s->hpg == 16) s->n_chunks = round_down8(2 * kCUs / s->n_hg);
     return MLA_OK;
 }
 
@@ -499,7 +500,7 @@ mla_status_t mla_decode_fp8_ex(int b, int h, int t_max, const void* q_prime, con
     DecodeParams p = split_params(q_prime, cache_codes, seqlens, out, lse, workspace, w, b, h, t_max,
                                   s.n_chunks, s.n_hg, softmax_scale);
     p.cache_scale = cache_scale;
-    return run_split(p, true, s.min_chunk, 1, false, cfg, (hipStream_t)stream,
+    return run_split(p, true, s.min_chunk, 1, bf16_variant_plans(s.hpg, s.variant), cfg, (hipStream_t)stream,
                      [&](const DecodeParams& q) { return launch_decode_bf16(q, s.hpg, s.variant, (hipStream_t)stream); });
 }
 

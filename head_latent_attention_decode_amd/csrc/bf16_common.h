@@ -87,6 +87,21 @@ struct IC {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x of lane l, x of lane l ^ 32): lanes l and l + 32 hold the two halves
+// of one head in the 32-wide MFMA layouts.  v_permlane32_swap exchanges the
+// upper 32 lanes of its first operand with the lower 32 lanes of its second,
+// so with x in both, each lane ends with its own value in one register and
+// its partner's in the other.  Written as inline asm because the compiler's
+// builtin returns its first result for both (the second result is lost); the
+// nops give the wait states around a permlane that the hazard recognizer
+// cannot see inside asm.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 template <int WH>
 struct Mfma;
 
@@ -131,6 +146,18 @@ __device__ __forceinline__ void block_work(int n_chunks, int n_hg, int& k, int& 
     const int slot = blockIdx.x >> 3;
     k = xcd * (n_chunks >> 3) + slot / n_hg;
     hg = slot % n_hg;
+}
+
+// Eight OCP e4m3 codes (first in the low byte) -> eight bf16, exact: every
+// e4m3 value is a bf16 value.
+__device__ __forceinline__ bf16x8_t cvt8_e4m3(unsigned long long codes)
+{
+    const unsigned lo = (unsigned)codes, hi = (unsigned)(codes >> 32);
+    const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
 // Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.

@@ -54,17 +54,6 @@ namespace {
 __device__ __forceinline__ int f8sw(int r) { return ((r >> 4) & 1) | ((r & 1) << 1); }
 __device__ __forceinline__ int f8chunk(int c, int sw) { return (c & ~3) | ((c & 3) ^ sw); }
 
-// Eight OCP e4m3 codes -> eight bf16 (exact: every e4m3 value is a bf16 value).
-__device__ __forceinline__ bf16x8_t cvt8(unsigned long long codes)
-{
-    const unsigned lo = (unsigned)codes, hi = (unsigned)(codes >> 32);
-    const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-}
-
 template <int WH, int HS, int TS, int NT, int STAGES>
 struct Tiling {
     static constexpr int NW = HS * TS;
@@ -349,7 +338,7 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
             auto k_frag = [&](int idx) -> bf16x8_t {
                 if (!FP8) return *(const LDS_AS bf16x8_t*)k_addr(idx);
                 const int ks = idx / T::SBLK, sb = idx % T::SBLK;
-                return cvt8(*(const LDS_AS unsigned long long*)(sg + k8off[sb] + k8x[sb][ks & 1] + 64 * (ks >> 1)));
+                return cvt8_e4m3(*(const LDS_AS unsigned long long*)(sg + k8off[sb] + k8x[sb][ks & 1] + 64 * (ks >> 1)));
             };
             acc_t sacc[T::SBLK][2];
 #pragma unroll
@@ -436,7 +425,7 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
                     typedef int v2i_t __attribute__((ext_vector_type(2)));
                     const v2i_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (LDS_AS v2i_t*)(sg + v8off + v8x[mb & 3] + 64 * (mb >> 2)));
-                    return cvt8(__builtin_bit_cast(unsigned long long, c));
+                    return cvt8_e4m3(__builtin_bit_cast(unsigned long long, c));
                 }
                 const int q = mb % NQV;
                 const int blk = (mb / NQV) * 256 + u * TPU * 1024;
@@ -774,9 +763,7 @@ __global__ __launch_bounds__(P * 128) void decode_pair_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 3; i < 16; ++i) tm = fmaxf(tm, sc[i]);
             // the head's other lane group is lane ^ 32
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, tm),
-                                                             __builtin_bit_cast(unsigned, tm), false, false);
-            sm_tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
+            sm_tmax = max_xor32(tm) * c2;
         };
         auto sm_rescale = [&]() {
             const float m_new = fmaxf(m_run, sm_tmax);
@@ -978,6 +965,8 @@ constexpr LaunchFn variant_launcher()
     if constexpr (FP8) {
         if constexpr (v.family == KernelFamily::Tiled && v.fp8_name != nullptr)
             return &launch_variant_fp8<v.targs[0], v.targs[1], v.targs[2], v.targs[3], v.targs[4]>;
+        else if constexpr (v.family == KernelFamily::Wide && v.fp8_name != nullptr)
+            return &launch_decode_wide_fp8;
         else
             return nullptr;
     } else if constexpr (v.family == KernelFamily::Tiled) {

@@ -336,9 +336,7 @@ __device__ __forceinline__ void colsplit_body(const DecodeParams& p)
                 for (int e = 3; e < 16; ++e) tm = fmaxf(tm, s[e]);
                 sm_tmax = tm;
             } else if (piece == 1) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, sm_tmax),
-                                                                 __builtin_bit_cast(unsigned, sm_tmax), false, false);
-                sm_tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
+                sm_tmax = max_xor32(sm_tmax) * c2;
                 sm_mnew = fmaxf(m_run, sm_tmax);
             } else if (piece == 2) {
                 int sm_flag = 0;

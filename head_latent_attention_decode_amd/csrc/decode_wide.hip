@@ -381,9 +381,7 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
             float tm = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
             for (int e = 3; e < 16; ++e) tm = fmaxf(tm, sacc[e]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, tm),
-                                                             __builtin_bit_cast(unsigned, tm), false, false);
-            const float tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c2;
+            const float tmax = max_xor32(tm) * c2;
             const float m_new = fmaxf(m_run, tmax);
             if (i == 0) {
                 m_run = m_new;  // first tile: nothing accumulated yet

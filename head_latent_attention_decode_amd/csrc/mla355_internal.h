@@ -142,6 +142,11 @@ hipError_t launch_decode_wide_causal(const DecodeParams& p, hipStream_t stream);
 // Column-split, software-pipelined bf16 kernel for groups of 128 heads.
 hipError_t launch_decode_colsplit(const DecodeParams& p, hipStream_t stream);
 
+// fp8-cache form of the 128-head wide kernel: queries quantised to e4m3 per
+// (batch row, head) on entry, scores on FP8 MFMAs, weighted sum on bf16 ones
+// (contiguous cache, one query token per row).
+hipError_t launch_decode_wide_fp8(const DecodeParams& p, hipStream_t stream);
+
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(long long n_rows, const void* x, void* codes, float* scale,

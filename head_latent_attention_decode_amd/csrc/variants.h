@@ -11,7 +11,7 @@ namespace mla355 {
 enum class KernelFamily {
     Tiled,  // decode_bf16_kernel<WH, HS, TS, NT, STAGES, FP8>
     Pair,   // decode_pair_kernel<P, STAGES>
-    Wide,   // decode_wide_kernel<NW, STAGES, PAGED>
+    Wide,   // decode_wide_kernel<NW, STAGES, PAGED>; fp8 cache: decode_wide_fp8_kernel (128 heads)
     Split,  // decode_colsplit_kernel<PAGED>: 128 heads, weighted sum split by columns
 };
 
@@ -52,7 +52,7 @@ inline constexpr VariantInfo kVariantInfo[] = {
     {128, 3, 32, KernelFamily::Wide, {4, 3}, "decode_wide_kernel<4, 3, false>", "decode_wide_kernel<4, 3, true>",
      nullptr, true},
     {128, 4, 32, KernelFamily::Wide, {4, 2}, "decode_wide_kernel<4, 2, false>", "decode_wide_kernel<4, 2, true>",
-     nullptr, true},
+     "decode_wide_fp8_kernel", true},
     {128, 5, 32, KernelFamily::Wide, {4, 4}, "decode_wide_kernel<4, 4, false>", "decode_wide_kernel<4, 4, true>",
      nullptr, false},
     {64, 5, 32, KernelFamily::Wide, {2, 3}, "decode_wide_kernel<2, 3, false>", "decode_wide_kernel<2, 3, true>",

@@ -79,3 +79,24 @@ def quantize_rows(x):
 def dequantize(codes, scale) -> np.ndarray:
     """fp64 rows: e4m3_value(codes) * scale (exact in fp64)."""
     return decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_query(q):
+    """Per-(row, head) query quantiser of the FP8-MFMA attention path (the
+    library's form; the pages define none).  q: array-like [..., 576] (bf16
+    values widened exactly).  Per vector, in fp32: amax = max|q|,
+    sigma = amax / 448, inv = 448 / amax (0 when amax is 0), and every code is
+    the e4m3 value nearest to clamp(q * inv, -448, 448), ties to the even
+    code.  Returns (codes uint8 [..., 576], sigma fp32 [...]); the dequantised
+    query is e4m3_value(code) * sigma."""
+    if hasattr(q, "detach"):
+        import torch
+        q = q.detach().to(device="cpu", dtype=torch.float32).numpy()
+    qf = np.asarray(q, dtype=np.float32)
+    amax = np.max(np.abs(qf), axis=-1).astype(np.float32)
+    sigma = (amax / np.float32(MAX_FINITE)).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = np.where(amax > 0, np.float32(MAX_FINITE) / safe, np.float32(0.0)).astype(np.float32)
+    x = (qf * inv[..., None]).astype(np.float32)
+    x = np.clip(x, -MAX_FINITE, MAX_FINITE).astype(np.float32)
+    return encode(x), sigma

@@ -311,6 +311,15 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int heads_per_group, int va
         walk_split(p, Shape{32 * v->targs[0], 32, true, true, 2, row_bytes});
         return hipSuccess;
     case KernelFamily::Wide:
+        if (fp8) {
+            // decode_wide_fp8_kernel: 128 heads, 32-token tiles of e4m3 rows
+            // and their scales, plan in LDS when it fits; contiguous cache only
+            if (p.plan_in_kernel && (p.b > kPlanLdsRows || p.n_chunks > kPlanLdsChunks))
+                return hipErrorInvalidValue;
+            if (p.block_table != nullptr || p.q_len != 1) return hipErrorInvalidValue;
+            walk_split(p, Shape{128, 32, true, true, 2, row_bytes});
+            return hipSuccess;
+        }
         return wide_launch(p, v->targs[0], v->targs[1], [&](const Shape& s) { walk_split(p, s); });
     case KernelFamily::Split:
         if (p.plan_in_kernel && (p.b > kPlanLdsRows || p.n_chunks > kPlanLdsChunks)) return hipErrorInvalidValue;

@@ -204,11 +204,21 @@ def test_fp8_validation_and_queries(mla):
                    ({"b": 0}, 1), ({"t": -1}, 1), ({"scale": -1.0}, 1), ({"wsb": 100}, 3),
                    ({"ws": A + 128}, 1), ({"b": 1 << 20, "t": 1 << 12}, 1)):
         assert dec(**kw) == st, kw
-    # only the 16-heads-per-group kernel reads e4m3 codes
+    # two kernels read e4m3 codes: the 16-head one (up to 64 heads by default)
+    # and the 128-head FP8-MFMA one (more heads)
     assert mla.mla_decode_fp8_kernel_name(16) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
-    assert mla.mla_decode_fp8_kernel_name(128) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
-    assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 128}) is None
+    assert mla.mla_decode_fp8_kernel_name(64) == "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
+    assert mla.mla_decode_fp8_kernel_name(65) == "decode_wide_fp8_kernel"
+    assert mla.mla_decode_fp8_kernel_name(128) == "decode_wide_fp8_kernel"
+    assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 128}) == "decode_wide_fp8_kernel"
+    assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 16}) == \
+        "decode_bf16_kernel<16, 1, 2, 32, 2, true>"
+    assert mla.mla_decode_fp8_kernel_name(128, {"heads_per_group": 128, "variant": 3}) is None
     assert mla.mla_decode_fp8_kernel_name(16, {"heads_per_group": 16, "variant": 2}) is None
+    assert mla.mla_decode_fp8_kernel_name(64, {"heads_per_group": 64}) is None
+    # the 128-head kernel: one workgroup per CU, the bf16 schedule's chunks
+    assert mla.mla_decode_fp8_workspace_bytes(64, 128, 4096) == \
+        mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
     # two resident workgroups per CU: twice the chunks of the bf16 schedule
     assert mla.mla_decode_fp8_workspace_bytes(128, 16, 8192) == \
         mla.mla_decode_workspace_bytes(torch.bfloat16, 128, 16, 8192, {"n_chunks": 512})

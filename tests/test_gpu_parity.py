@@ -186,6 +186,49 @@ def test_bf16_running_max_growth(mla, h, cfg):
         check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
 
 
+TILE_MAX_CASES = [
+    (128, None), (128, {"heads_per_group": 128, "variant": 6}), (64, {"heads_per_group": 64, "variant": 6}),
+    (64, {"heads_per_group": 64, "variant": 3}), (32, {"heads_per_group": 32, "variant": 4}),
+    (128, {"heads_per_group": 128, "variant": 2}),
+]
+
+
+@pytest.mark.parametrize("h,cfg", TILE_MAX_CASES, ids=[_case_id(c) for c in TILE_MAX_CASES])
+def test_bf16_tile_max_spans_both_lane_halves(mla, h, cfg):
+    # In the 32-wide MFMA layouts lane l holds tokens 8i + 0..3 of a head and
+    # lane l + 32 tokens 8i + 4..7.  Here the second kind score about 1280
+    # above the first (q' and k agree in channel 575), so a tile maximum
+    # taken over one lane's tokens only sits ~133 below the true one in base 2
+    # and exp2 overflows; the true maximum keeps every probability <= 1.
+    lens = [64, 33, 700]
+    w = workloads.make_custom(len(lens), h, lens, seed=90 + h, device="cuda", poison=False)
+    t = torch.arange(w.t_max, device="cuda")
+    w.cache[:, :, 575] = torch.where((t % 8) >= 4, 40.0, 0.0).to(torch.bfloat16)[None, :]
+    w.q_prime[:, :, 575] = 32.0
+    workloads.poison_tail(w.cache, w.seqlens)
+    for extra in ({}, {"n_chunks": 8}):
+        c = dict(cfg or {})
+        c.update(extra)
+        out, lse = _run(mla, w, c or None)
+        check_decode(w.q_prime, w.cache, w.seqlens, w.scale, out, lse, range(w.b))
+
+
+def test_fp8_wide_tile_max_spans_both_lane_halves(mla):
+    # the same construction through the FP8-MFMA kernel (its tile maximum and
+    # the per-head query maximum both combine the two lanes of a head)
+    h, lens = 128, [64, 33, 700]
+    w = workloads.make_custom(len(lens), h, lens, seed=95, device="cuda", poison=False)
+    t = torch.arange(w.t_max, device="cuda")
+    w.cache[:, :, 575] = torch.where((t % 8) >= 4, 40.0, 0.0).to(torch.bfloat16)[None, :]
+    w.q_prime[:, :, 575] = 32.0
+    codes, scale, deq = _fp8_from(w)
+    qd = _fp8_query_deq(w.q_prime)
+    ref_out, ref_lse = oracle.decode_latent(qd, deq, w.seqlens.cpu(), w.scale)
+    out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    check_fp8_mfma(out, lse, qd, deq, lens, w.scale, ref_out, ref_lse)
+
+
 def test_bf16_split_invariance_and_determinism(mla):
     w = workloads.make_custom(5, 128, [3000, 17, 4096, 1, 2500], seed=7, device="cuda")
     outs = []
@@ -389,8 +432,13 @@ def test_fp8_edges_every_output(mla, h):
     w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=500 + h, device="cuda")
     codes, scale, deq = _fp8_from(w)
     ref_out, ref_lse = oracle.decode_latent(w.q_prime.cpu(), deq, w.seqlens.cpu(), w.scale)
+    # the 16-head kernel (exact bf16 queries) also at more than 64 heads, where
+    # the automatic choice is the FP8-MFMA kernel
+    base = {"heads_per_group": 16} if h > 64 else {}
+    assert mla.mla_decode_fp8_kernel_name(h, base or None).startswith("decode_bf16_kernel<16")
     for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}):
-        out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=extra or None)
+        cfg = dict(base, **extra)
+        out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=cfg or None)
         torch.cuda.synchronize()
         assert_out(to_np(out), ref_out, BF16_OUT_REL, "out %s" % extra)
         assert_lse(to_np(lse), ref_lse, BF16_LSE_ABS)
@@ -412,6 +460,134 @@ def test_full_few_heads_fp8_b128_h16_T8192(mla):
     ref_out, ref_lse = oracle.decode_latent(w.q_prime[rows].cpu(), deq, w.seqlens[rows].cpu(), w.scale)
     assert_out(to_np(out[rows]), ref_out, BF16_OUT_REL)
     assert_lse(to_np(lse[rows]), ref_lse, BF16_LSE_ABS)
+
+
+# ------------------------------------------- fp8 cache, 128-head FP8-MFMA kernel
+
+def _fp8_query_deq(q_prime):
+    """The FP8-MFMA path's quantised queries (the oracle's quantiser, the same
+    fp32 steps the kernel takes), dequantised exactly in fp64."""
+    from oracle import fp8 as ofp8
+    codes, sigma = ofp8.quantize_query(q_prime.float().cpu().numpy())
+    return ofp8.decode(codes) * sigma[..., None].astype(np.float64)
+
+
+# The FP8 MFMA adds its 64 exact code products with less than fp32
+# precision: a probe of v_mfma_scale_f32_32x32x64_f8f6f4 on random codes put
+# the error of one score at up to 2^-15.4 of sum |a b|, and the large-score
+# test below at 2^-13.8.  The FP8-MFMA checks allow 2^-12 of
+# scale * sum_i |q8_i k_i| per score.
+FP8_MFMA_SUM_REL = 2.0 ** -12
+
+
+def check_fp8_mfma(out, lse, qdeq, kdeq, lens, scale, ref_out, ref_lse, extra_d=None, what="out"):
+    """out/lse of the FP8-MFMA kernel against the oracle fed the same query
+    and cache codes.  Each score may be off by d_t = 2^-12 * scale *
+    sum_i |q_i k_t,i|; with D = max_t d_t for a (row, head) the lse may move by
+    D and every softmax weight by a factor within [e^-2D, e^2D], so out by
+    (e^2D - 1) * max_t |v_t| per column -- on top of the bf16 bar.  extra_d
+    [b, h] adds to D (a further bounded score perturbation)."""
+    got_o, got_l = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(got_o)), "%s has non-finite values" % what
+    bar = BF16_OUT_REL * float(np.max(np.abs(ref_out)))
+    for r, L in enumerate(lens):
+        if L <= 0:
+            assert np.all(got_o[r] == 0) and np.all(np.isneginf(got_l[r]))
+            continue
+        k = kdeq[r, :L]
+        D = FP8_MFMA_SUM_REL * scale * (np.abs(qdeq[r]) @ np.abs(k).T).max(axis=1)   # [h]
+        if extra_d is not None:
+            D = D + extra_d[r]
+        vmax = np.abs(k[:, :512]).max(axis=0)
+        err = np.abs(got_o[r] - ref_out[r])
+        bound = np.expm1(2 * D)[:, None] * vmax[None, :] + bar
+        assert np.all(err <= bound), "%s row %d: max|err| %.3e beyond the bound" % (what, r, err.max())
+        lerr = np.abs(got_l[r] - ref_lse[r])
+        assert np.all(lerr <= D + BF16_LSE_ABS), "%s row %d: lse err %.3e" % (what, r, lerr.max())
+
+
+FP8_WIDE_CASES = [128, 100, 65, 256]
+
+
+@pytest.mark.parametrize("h", FP8_WIDE_CASES, ids=["h%d" % h for h in FP8_WIDE_CASES])
+def test_fp8_wide_every_output(mla, h):
+    # Query codes decided in fp32 on both sides: against the oracle fed the
+    # same codes (and the same cache codes), what is left is the bf16
+    # probabilities, fp32 accumulation and the bf16 output -- the bf16 bar.
+    w = workloads.make_custom(len(EDGE_LENS), h, EDGE_LENS, seed=800 + h, device="cuda")
+    codes, scale, deq = _fp8_from(w)
+    assert mla.mla_decode_fp8_kernel_name(h) == "decode_wide_fp8_kernel"
+    qd = _fp8_query_deq(w.q_prime)
+    ref_out, ref_lse = oracle.decode_latent(qd, deq, w.seqlens.cpu(), w.scale)
+    # 2560 chunks: more than the kernel plans in its own LDS (plan kernel)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}, {"n_chunks": 256}, {"n_chunks": 2560}):
+        out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=extra or None)
+        torch.cuda.synchronize()
+        check_fp8_mfma(out, lse, qd, deq, EDGE_LENS, w.scale, ref_out, ref_lse, what="out %s" % extra)
+        assert torch.all(out[EDGE_LENS.index(0)] == 0)
+        assert torch.all(torch.isneginf(lse[EDGE_LENS.index(0)]))
+        out2, lse2 = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=extra or None)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2), "not deterministic"
+
+
+def test_fp8_wide_running_max_growth(mla):
+    # The bf16 rescale construction on the fp8 path: scores that grow tile
+    # after tile for some heads (lazy rescale of the AGPR outputs), not for others.
+    h = 128
+    w = workloads.make_custom(4, h, [700, 257, 1000, 33], seed=61 + h, device="cuda", poison=False)
+    t = torch.arange(w.t_max, device="cuda", dtype=torch.float32)
+    w.cache[:, :, 575] = (0.25 * t).to(torch.bfloat16)[None, :]
+    slope = torch.tensor([16.0, 4.0, 1.0, 0.0, -4.0, 0.5, 8.0, -1.0], device="cuda")
+    per_head = slope[torch.arange(h, device="cuda") % 8]
+    per_head = torch.where((torch.arange(h, device="cuda") // 32) % 2 == 1, -per_head.abs(), per_head)
+    w.q_prime[:, :, 575] = per_head.to(torch.bfloat16)[None, :]
+    codes, scale, deq = _fp8_from(w)
+    qd = _fp8_query_deq(w.q_prime)
+    ref_out, ref_lse = oracle.decode_latent(qd, deq, w.seqlens.cpu(), w.scale)
+    for extra in ({}, {"n_chunks": 8}, {"n_chunks": 64}):
+        out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, config=extra or None)
+        torch.cuda.synchronize()
+        check_fp8_mfma(out, lse, qd, deq, [700, 257, 1000, 33], w.scale, ref_out, ref_lse, what="out %s" % extra)
+
+
+def test_fp8_wide_query_quantisation_bound(mla):
+    # Against the oracle with the exact bf16 queries (and the same cache
+    # codes).  Quantising a query moves its score with token t by
+    # d_t = scale * (q - q8) . k_t; with D = max_t |d_t| for a (row, head),
+    # every softmax weight moves by a factor within [e^-2D, e^2D], so
+    # |out - out_exact| <= (e^2D - 1) * max_t |v_t| per column and
+    # |lse - lse_exact| <= D.  Checked per (row, head), with D added to the
+    # FP8-MFMA allowance, on top of the bf16 bar.
+    h = 128
+    lens = [700, 1, 257, 64, 1000]
+    w = workloads.make_custom(len(lens), h, lens, seed=77, device="cuda")
+    codes, scale, deq = _fp8_from(w)
+    out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    q = w.q_prime.double().cpu().numpy()
+    qd = _fp8_query_deq(w.q_prime)
+    ref_out, ref_lse = oracle.decode_latent(q, deq, w.seqlens.cpu(), w.scale)
+    d_quant = np.zeros((len(lens), h))
+    for r, L in enumerate(lens):
+        d_quant[r] = (w.scale * np.abs((q[r] - qd[r]) @ deq[r, :L].T)).max(axis=1)
+    print("largest score move from quantising the queries: %.4f" % d_quant.max())
+    check_fp8_mfma(out, lse, qd, deq, lens, w.scale, ref_out, ref_lse, extra_d=d_quant)
+
+
+def test_full_dsv3_decode_fp8_b64_h128_T4096(mla):
+    # the 128-head configuration with its cache quantised on the GPU; sampled
+    # rows against the oracle fed the same cache and query codes
+    from oracle import fp8 as ofp8
+    w = workloads.make(2, device="cuda", poison=False)
+    codes, scale = mla.mla_quantize_cache_fp8(w.cache)
+    out, lse = mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = [0, 1, 33, 63]
+    deq = ofp8.dequantize(codes[rows].cpu().numpy(), scale[rows].cpu().numpy())
+    qd = _fp8_query_deq(w.q_prime[rows])
+    ref_out, ref_lse = oracle.decode_latent(qd, deq, w.seqlens[rows].cpu(), w.scale)
+    check_fp8_mfma(out[rows], lse[rows], qd, deq, w.seqlens[rows].tolist(), w.scale, ref_out, ref_lse)
 
 
 # ---------------------------------------------------------------- absorbs, bf16

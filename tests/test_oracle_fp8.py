@@ -65,3 +65,44 @@ def test_quantiser_properties():
     # signs survive
     nz = x != 0
     assert np.all(np.sign(deq[nz]) == np.sign(x[nz]))
+
+
+def test_query_quantiser_properties():
+    # per-vector (last axis) form of the FP8-MFMA attention path
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 5, 576)).astype(np.float32)
+    q[1, 2] = 0.0                                            # an all-zero query
+    q[2, 4, 17] = -40.0                                      # one large entry
+    codes, sigma = fp8.quantize_query(q)
+    assert codes.shape == q.shape and codes.dtype == np.uint8 and sigma.shape == (3, 5)
+    amax = np.abs(q).max(axis=-1)
+    np.testing.assert_array_equal(sigma, (amax / np.float32(448)).astype(np.float32))
+    assert sigma[1, 2] == 0 and np.all(codes[1, 2] == 0)
+    # each vector's largest magnitude lands on +-448 with its sign
+    assert codes[2, 4, 17] == 0xFE
+    for i in range(3):
+        for j in range(5):
+            if (i, j) != (1, 2):
+                assert codes[i, j, np.abs(q[i, j]).argmax()] & 0x7F == 0x7E
+    # dequantised error: at most half a step of the e4m3 grid (the fp32
+    # product q * (448 / amax) is within one rounding of q / sigma)
+    deq = fp8.decode(codes) * sigma[..., None].astype(np.float64)
+    bound = np.maximum(np.abs(q) * 2.0 ** -4, sigma[..., None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(np.abs(deq - q) <= bound * (1 + 1e-5))
+    assert np.all(np.sign(deq[q != 0]) == np.sign(q[q != 0]))
+
+
+def test_query_quantiser_exact_grid():
+    # values on the e4m3 grid times 2^-5 with a largest magnitude of 448 * 2^-5
+    # (= 14): 448 / 14 = 32 exactly, so every product is a grid value and the
+    # codes come back unchanged (a divide-instead-of-multiply or a wrong
+    # constant would move them)
+    rng = np.random.default_rng(10)
+    finite = np.array([c for c in range(256) if np.isfinite(fp8.VALUES[c])], np.uint8)
+    c = rng.choice(finite, size=576).astype(np.uint8)
+    c[0] = 0x7E
+    q = (fp8.VALUES[c] * 2.0 ** -5).astype(np.float32)
+    codes, sigma = fp8.quantize_query(q)
+    assert sigma == np.float32(14.0 / 448.0)
+    # negative zero and zero both decode to 0: compare values, not bytes
+    np.testing.assert_array_equal(fp8.VALUES[codes], fp8.VALUES[c])
