@@ -231,6 +231,7 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         }
         auto tile_ptr = [&](int tile) -> const unsigned char* {
             if (!PAGED) return seg_base + (size_t)tile * T::N * kRowBytesBf16;
+            if (tile >= n_tiles) return cg;  // an empty refill: no block-table read
             // a scalar load: its wait does not queue behind the tile DMAs in flight
             const int e = min(max(*(cint32_t*)(p.block_table + (size_t)r * p.max_blocks + pg_blk), 0),
                               p.num_blocks - 1);
@@ -246,10 +247,14 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         // DMA instruction `li` (0 .. LOADS-1) of this wave's share of `tile`
         // (first row at tptr) into stage SC.  Rows past the segment end
         // re-read its last row (the scores of those slots are masked), so
-        // every access stays inside the rows of this segment.
+        // every access stays inside the rows of this segment.  A tile at or
+        // past n_tiles gets an empty resource: the instructions still issue
+        // (a free stage receives zeros, no memory is read), so every step
+        // issues the same DMA count, the waits below are constants and the
+        // compiler's own DMA bookkeeping adds no wait of its own.
         auto issue_load = [&](auto SC, const unsigned char* tptr, int tile, int li) {
             const int t0 = tile * T::N;
-            const int last = min(T::N, seg_len - t0) - 1;
+            const int last = (tile < n_tiles ? min(T::N, seg_len - t0) : 0) - 1;
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)tptr, (short)0, (last + 1) * kRowBytesBf16, kBufferFlags);
             lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
@@ -277,22 +282,14 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         };
         // Wait until this wave's share of tile t has landed.  Tile 0 goes out
         // before the queries, tiles 1 .. STAGES-2 right after them, and step i
-        // refills tile i+STAGES-1, so the tiles issued after t are t+1 ..
-        // min(t+STAGES-2, n_tiles-1) (at step 0 the queries sit between tile 0
-        // and tile 1 and are waited for too, which the first MFMA needs anyway).
-        auto wait_tile = [&](int t) {
-            const int after = min(STAGES - 2, n_tiles - 1 - t);
-            if (STAGES > 3 && after >= 2)
-                wait_vmcnt<(STAGES > 3 ? 2 : 0) * T::LOADS>();
-            else if (STAGES > 2 && after >= 1)
-                wait_vmcnt<(STAGES > 2 ? 1 : 0) * T::LOADS>();
-            else
-                wait_vmcnt<0>();
-        };
+        // refills tile i+STAGES-1 (real or empty), so the tiles issued after t
+        // are always t+1 .. t+STAGES-2 (at step 0 the queries sit between tile
+        // 0 and tile 1 and are waited for too, which the first MFMA needs anyway).
+        auto wait_tile = [&]() { wait_vmcnt<(STAGES - 2) * T::LOADS>(); };
 
         // Tile 0 first: the queries are as large as a tile, and the first
         // score MFMA needs both.
-        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
+        issue_tile(IC<0>{}, 0);
         // Queries (B operand): lane -> head hl, channels 16j + 8grp .. +7 of step j.
         // A lane past the last head reads head 0's query instead (finite values,
         // results never stored), so nothing waits on the loads before the
@@ -304,8 +301,8 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
 #pragma unroll
             for (int j = 0; j < T::KS; ++j) qf[j] = qrow[2 * j + grp];
         }
-        if (STAGES > 2 && 1 < n_tiles) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
-        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
+        if (STAGES > 2) issue_tile(IC<(STAGES > 2 ? 1 : 0)>{}, 1);
+        if (STAGES > 3) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
 
         acc_t o[T::MBLK];
 #pragma unroll
@@ -332,18 +329,15 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
             constexpr int S = decltype(SC)::value;
             constexpr int SR = (S + STAGES - 1) % STAGES;  // stage of tile i-1 = refill target
             lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
-            const bool refill = i + STAGES - 1 < n_tiles;
             // the refill's address first: a paged lookup completes during the barrier
-            const unsigned char* rptr = refill ? tile_ptr(i + STAGES - 1) : nullptr;
-            wait_tile(i);
+            const unsigned char* rptr = tile_ptr(i + STAGES - 1);
+            wait_tile();
             lds_exchange_barrier();  // tile i visible to all; everyone is done with tile i-1
 
-            // ---- scores: S^T = K . Q'^T, refill DMA spread over the first steps
-            // (two copies of the loop, with and without the refill, so that no
-            // branch sits between the MFMAs)
+            // ---- scores: S^T = K . Q'^T, the refill DMA of tile i+STAGES-1
+            // spread over the first steps
             acc_t sacc;
-            auto scores = [&](auto RF) {
-                constexpr bool REFILL = decltype(RF)::value != 0;
+            {
                 constexpr int PF = 4;
                 bf16x8_t kring[PF];
 #pragma unroll
@@ -353,14 +347,10 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
                     const bf16x8_t kf = kring[j % PF];
                     if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
                     sacc = (j == 0) ? M::mma(kf, qf[j], (acc_t){}) : M::mma(kf, qf[j], sacc);
-                    if (REFILL && j < T::LOADS) issue_load(IC<SR>{}, rptr, i + STAGES - 1, j);
+                    if (j < T::LOADS) issue_load(IC<SR>{}, rptr, i + STAGES - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            };
-            if (refill)
-                scores(IC<1>{});
-            else
-                scores(IC<0>{});
+            }
 
             // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
             const int tvalid = __builtin_amdgcn_readfirstlane(seg_len - i * T::N);
@@ -430,11 +420,21 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
             }
         };
 
+        // The steps form one chain (each reachable only from the one before),
+        // so every path into a step carries the same DMA queue.
         for (int i0 = 0; i0 < n_tiles; i0 += STAGES) {
             step(IC<0>{}, i0);
-            if (i0 + 1 < n_tiles) step(IC<1 % STAGES>{}, i0 + 1);
-            if (STAGES > 2 && i0 + 2 < n_tiles) step(IC<(STAGES > 2 ? 2 : 0)>{}, i0 + 2);
-            if (STAGES > 3 && i0 + 3 < n_tiles) step(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
+            if (i0 + 1 >= n_tiles) break;
+            step(IC<1 % STAGES>{}, i0 + 1);
+            if (i0 + 2 >= n_tiles) break;
+            if constexpr (STAGES > 2) {
+                step(IC<(STAGES > 2 ? 2 : 0)>{}, i0 + 2);
+                if (i0 + 3 >= n_tiles) break;
+            }
+            if constexpr (STAGES > 3) {
+                step(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
+                if (i0 + 4 >= n_tiles) break;
+            }
         }
 
         // ---- segment epilogue ----------------------------------------------
@@ -445,7 +445,8 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
         // LDS (the tile ring is free once every wave is past the last tile)
         // and stores whole 512-byte half rows.
         l_run += __shfl_xor(l_run, 32, 64);
-        lds_exchange_barrier();  // no DMA is in flight after the last tile
+        wait_vmcnt<0>();         // the empty refills past the last tile have landed
+        lds_exchange_barrier();
         {
             // The lane's head and column group are derived again here from the
             // thread index (opaque to the compiler) instead of being kept live

@@ -168,17 +168,32 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
     // u = 2grp ^ sw8(rr) the first sits at chunk position 4j ^ u, i.e. for
     // j = 4a + b at rr*512 + 16(u & 3) + 64(b ^ (u >> 2)) + 256a, and the
     // second at that position ^ 1.
-    const int rr = lane & 31;
-    const int ku = (2 * grp) ^ sw8(rr);
-    int koff[4];
+    // The offsets are recomputed where they are used, from a thread index
+    // the compiler cannot see through, so that none of them stays live across
+    // the tile loop (every register is taken there).
+    auto opaque_lane = [&]() {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t & 63;
+    };
+    struct KOffsets {
+        int koff[4], kflip, kb0, kb1, soff;
+    };
+    auto k_offsets = [&]() {
+        KOffsets o;
+        const int l = opaque_lane();
+        const int rr = l & 31, g = l >> 5;
+        const int ku = (2 * g) ^ sw8(rr);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) koff[b] = rr * 512 + 16 * (ku & 3) + 64 * (b ^ (ku >> 2));
-    const int kflip = (ku & 1) ? -16 : 16;
-    // Step 8 (channels 512..575): region B, chunk c of row r at c ^ ((r >> 2) & 3).
-    const int kb0 = T::B_OFF + rr * 64 + 16 * ((2 * grp) ^ ((rr >> 2) & 3));
-    const int kb1 = T::B_OFF + rr * 64 + 16 * ((2 * grp + 1) ^ ((rr >> 2) & 3));
-    // Token scales of the lane's accumulator entries (tokens 8q + 4grp .. +3).
-    const int soff = T::SCL_OFF + 16 * grp;
+        for (int b = 0; b < 4; ++b) o.koff[b] = rr * 512 + 16 * (ku & 3) + 64 * (b ^ (ku >> 2));
+        o.kflip = (ku & 1) ? -16 : 16;
+        // Step 8 (channels 512..575): region B, chunk c of row r at c ^ ((r >> 2) & 3).
+        o.kb0 = T::B_OFF + rr * 64 + 16 * ((2 * g) ^ ((rr >> 2) & 3));
+        o.kb1 = T::B_OFF + rr * 64 + 16 * ((2 * g + 1) ^ ((rr >> 2) & 3));
+        // Token scales of the lane's accumulator entries (tokens 8q + 4g .. +3).
+        o.soff = T::SCL_OFF + 16 * g;
+        return o;
+    };
     // Weighted sum: ds_read_b64_tr_b8 hands output lane i of a 16-lane group
     // byte i % 8 of source lanes 2e + i / 8 (e = 0..7), so source lane pair e
     // supplies the 16 bytes of k slot e.  Group G = lane >> 4 builds the A
@@ -190,14 +205,19 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
     // 2mb ^ w, w = (G & 1) ^ sw8(t0): for mb = 8a + b at
     // t0*512 + 16(w & 1) + 8(s & 1) + 32(b ^ (w >> 1)) + 256a (+8192 for the
     // second half).
-    int voff[8];
-    {
-        const int G = lane >> 4, s = lane & 15, e = s >> 1;
+    struct VOffsets {
+        int voff[8];
+    };
+    auto v_offsets = [&]() {
+        VOffsets o;
+        const int l = opaque_lane();
+        const int G = l >> 4, sl = l & 15, e = sl >> 1;
         const int t0 = 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
         const int w = (G & 1) ^ sw8(t0);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) voff[b] = t0 * 512 + 16 * (w & 1) + 8 * (s & 1) + 32 * (b ^ (w >> 1));
-    }
+        for (int b = 0; b < 8; ++b) o.voff[b] = t0 * 512 + 16 * (w & 1) + 8 * (sl & 1) + 32 * (b ^ (w >> 1));
+        return o;
+    };
 
     while (true) {
         const int row_lo = pl_cu(r);
@@ -215,27 +235,34 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
         // DMA instruction `li` (0 .. LOADS-1) of this wave's share of `tile`
         // into stage SC.  Rows past the segment end re-read its last row
         // (their scores are masked), so every code access stays inside the
-        // segment; scales past the end read as 0 (outside the resource).
+        // segment; scales past the end read as 0 (outside the resource).  A
+        // tile past the last one gets an empty resource: the instructions
+        // are still issued (zeros land in a free stage, no memory is read),
+        // so every step issues the same DMA count and the compiler's own
+        // waits need not assume a shorter queue.
         auto issue_load = [&](auto SC, int tile, int li) {
             const int t0 = tile * T::N;
-            const int last = min(T::N, seg_len - t0) - 1;
+            // uniform (a scalar value: a resource built from a vector register
+            // would need a loop over lanes)
+            const int last = __builtin_amdgcn_readfirstlane((tile < n_tiles ? min(T::N, seg_len - t0) : 0) - 1);
             lds_byte* st = stage_lds<T::TILE_BYTES, decltype(SC)::value>();
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(seg_base + (size_t)t0 * T::ROW8), (short)0, (last + 1) * T::ROW8, kBufferFlags);
+            const int ln = opaque_lane();
             if (li < T::LOADS_A) {
                 // rows 2q, 2q + 1 (lanes 0..31, 32..63); lane position l & 31
                 // holds logical chunk (l & 31) ^ sw8(row)
                 const int q = wave + li * T::NW;
-                const int row = 2 * q + (lane >> 5);
+                const int row = 2 * q + (ln >> 5);
                 const int srow = min(row, last);
-                const int c = (lane & 31) ^ sw8(row);
+                const int c = (ln & 31) ^ sw8(row);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + q * 1024), 16,
                                                          (unsigned)(srow * T::ROW8 + c * 16), 0, 0, 0);
             } else if (wave < 2) {
                 // region B rows 16 wave .. +15: lane -> row 16 wave + l / 4, position l % 4
-                const int row = 16 * wave + (lane >> 2);
+                const int row = 16 * wave + (ln >> 2);
                 const int srow = min(row, last);
-                const int c = (lane & 3) ^ ((row >> 2) & 3);
+                const int c = (ln & 3) ^ ((row >> 2) & 3);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::B_OFF + wave * 1024), 16,
                                                          (unsigned)(srow * T::ROW8 + 512 + c * 16), 0, 0, 0);
             } else {
@@ -246,28 +273,16 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
                 const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(seg_scale + t0), (short)0, (last + 1) * 4, kBufferFlags);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (LDS_AS void*)(st + T::SCL_OFF), 4,
-                                                         (unsigned)(lane * 4), 0, 0, 0);
+                                                         (unsigned)(ln * 4), 0, 0, 0);
             }
         };
         auto issue_tile = [&](auto SC, int tile) {
 #pragma unroll
             for (int li = 0; li < T::LOADS; ++li) issue_load(SC, tile, li);
         };
-        // Wait until this wave's share of tile t has landed: the tiles issued
-        // after it are t+1 .. min(t+STAGES-2, n_tiles-1).
-        auto wait_tile = [&](int t) {
-            const int after = min(STAGES - 2, n_tiles - 1 - t);
-            if (STAGES > 5 && after >= 4)
-                wait_vmcnt<(STAGES > 5 ? 4 : 0) * T::LOADS>();
-            else if (STAGES > 4 && after >= 3)
-                wait_vmcnt<(STAGES > 4 ? 3 : 0) * T::LOADS>();
-            else if (STAGES > 3 && after >= 2)
-                wait_vmcnt<(STAGES > 3 ? 2 : 0) * T::LOADS>();
-            else if (STAGES > 2 && after >= 1)
-                wait_vmcnt<(STAGES > 2 ? 1 : 0) * T::LOADS>();
-            else
-                wait_vmcnt<0>();
-        };
+        // Wait until this wave's share of tile t has landed: tiles t+1 ..
+        // t+STAGES-2 (real or empty) were issued after it.
+        auto wait_tile = [&]() { wait_vmcnt<(STAGES - 2) * T::LOADS>(); };
 
         // Queries first (bf16, lane -> head hl, channels 64j + 32grp .. +31 of
         // step j), then the first STAGES-1 tiles, which land while the
@@ -280,11 +295,11 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) qb[4 * j + v] = qrow[8 * j + 4 * grp + v];
         }
-        if (0 < n_tiles) issue_tile(IC<0>{}, 0);
-        if (1 < n_tiles) issue_tile(IC<1>{}, 1);
-        if (STAGES > 3 && 2 < n_tiles) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
-        if (STAGES > 4 && 3 < n_tiles) issue_tile(IC<(STAGES > 4 ? 3 : 0)>{}, 3);
-        if (STAGES > 5 && 4 < n_tiles) issue_tile(IC<(STAGES > 5 ? 4 : 0)>{}, 4);
+        issue_tile(IC<0>{}, 0);
+        issue_tile(IC<1>{}, 1);
+        if (STAGES > 3) issue_tile(IC<(STAGES > 3 ? 2 : 0)>{}, 2);
+        if (STAGES > 4) issue_tile(IC<(STAGES > 4 ? 3 : 0)>{}, 3);
+        if (STAGES > 5) issue_tile(IC<(STAGES > 5 ? 4 : 0)>{}, 4);
 
         // Quantise: the head's max |q'| over its 576 channels (this lane holds
         // half of them, the lane 32 away the other half).
@@ -329,31 +344,30 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
             constexpr int S = decltype(SC)::value;
             constexpr int SR = (S + STAGES - 1) % STAGES;  // stage of tile i-1 = refill target
             lds_byte* tb = stage_lds<T::TILE_BYTES, S>();
-            const bool refill = i + STAGES - 1 < n_tiles;
-            wait_tile(i);
+            wait_tile();
             lds_exchange_barrier();  // tile i visible to all; everyone is done with tile i-1
 
+            const KOffsets ko = k_offsets();
             f32x4_t sc[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sc[q] = *(const LDS_AS f32x4_t*)(tb + soff + 32 * q);
+            for (int q = 0; q < 4; ++q) sc[q] = *(const LDS_AS f32x4_t*)(tb + ko.soff + 32 * q);
 
-            // ---- scores: S^T = K . Q'^T on the FP8 cores, refill DMA spread
-            // over the first steps (two copies of the loop, with and without it)
+            // ---- scores: S^T = K . Q'^T on the FP8 cores, the refill DMA of
+            // tile i+STAGES-1 spread over the first steps
             acc_t sacc;
             auto k_frag = [&](int j) -> i32x8_t {
                 i32x4_t lo, hi;
                 if (j < 8) {
-                    const int o0 = koff[j & 3] + 256 * (j >> 2);
+                    const int o0 = ko.koff[j & 3] + 256 * (j >> 2);
                     lo = *(const LDS_AS i32x4_t*)(tb + o0);
-                    hi = *(const LDS_AS i32x4_t*)(tb + o0 + kflip);
+                    hi = *(const LDS_AS i32x4_t*)(tb + o0 + ko.kflip);
                 } else {
-                    lo = *(const LDS_AS i32x4_t*)(tb + kb0);
-                    hi = *(const LDS_AS i32x4_t*)(tb + kb1);
+                    lo = *(const LDS_AS i32x4_t*)(tb + ko.kb0);
+                    hi = *(const LDS_AS i32x4_t*)(tb + ko.kb1);
                 }
                 return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             };
-            auto scores = [&](auto RF) {
-                constexpr bool REFILL = decltype(RF)::value != 0;
+            {
                 constexpr int PF = 2;
                 i32x8_t kring[PF];
 #pragma unroll
@@ -366,15 +380,11 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
                         sacc = score8_first(kf, q8[0], one);
                     else
                         score8_acc(sacc, kf, q8[j], one);
-                    if (REFILL && j < T::LOADS) issue_load(IC<SR>{}, i + STAGES - 1, j);
+                    if (j < T::LOADS) issue_load(IC<SR>{}, i + STAGES - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 score8_wait(sacc);
-            };
-            if (refill)
-                scores(IC<1>{});
-            else
-                scores(IC<0>{});
+            }
 
             // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
             float x[16];
@@ -423,10 +433,11 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
             // ---- weighted sum: O^T += V^T . P^T (codes converted to bf16)
             constexpr int NPV = 2 * T::MBLK;
             constexpr int PFV = 4;
+            const VOffsets vo = v_offsets();
             auto v_frag = [&](int idx) -> i32x2_t {
                 const int u = idx / T::MBLK, mb = idx % T::MBLK;
                 return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (LDS_AS i32x2_t*)(tb + voff[mb & 7] + 8192 * u + 256 * (mb >> 3)));
+                    (LDS_AS i32x2_t*)(tb + vo.voff[mb & 7] + 8192 * u + 256 * (mb >> 3)));
             };
             i32x2_t vring[PFV];
 #pragma unroll
@@ -442,13 +453,30 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
             }
         };
 
-        for (int i0 = 0; i0 < n_tiles; i0 += STAGES) {
+        // The steps form one chain (each reachable only from the one before),
+        // so the compiler's own DMA bookkeeping sees the same queue on every
+        // path into a step and adds no wait of its own.  n_tiles >= 1.
+        for (int i0 = 0;; i0 += STAGES) {
             step(IC<0>{}, i0);
-            if (i0 + 1 < n_tiles) step(IC<1>{}, i0 + 1);
-            if (STAGES > 2 && i0 + 2 < n_tiles) step(IC<(STAGES > 2 ? 2 : 0)>{}, i0 + 2);
-            if (STAGES > 3 && i0 + 3 < n_tiles) step(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
-            if (STAGES > 4 && i0 + 4 < n_tiles) step(IC<(STAGES > 4 ? 4 : 0)>{}, i0 + 4);
-            if (STAGES > 5 && i0 + 5 < n_tiles) step(IC<(STAGES > 5 ? 5 : 0)>{}, i0 + 5);
+            if (i0 + 1 >= n_tiles) break;
+            step(IC<1>{}, i0 + 1);
+            if (i0 + 2 >= n_tiles) break;
+            if constexpr (STAGES > 2) {
+                step(IC<(STAGES > 2 ? 2 : 0)>{}, i0 + 2);
+                if (i0 + 3 >= n_tiles) break;
+            }
+            if constexpr (STAGES > 3) {
+                step(IC<(STAGES > 3 ? 3 : 0)>{}, i0 + 3);
+                if (i0 + 4 >= n_tiles) break;
+            }
+            if constexpr (STAGES > 4) {
+                step(IC<(STAGES > 4 ? 4 : 0)>{}, i0 + 4);
+                if (i0 + 5 >= n_tiles) break;
+            }
+            if constexpr (STAGES > 5) {
+                step(IC<(STAGES > 5 ? 5 : 0)>{}, i0 + 5);
+                if (i0 + 6 >= n_tiles) break;
+            }
         }
 
         // ---- segment epilogue ----------------------------------------------
@@ -457,7 +485,8 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
         // 32 x 512 outputs at a time in its own ring stage (free once every
         // wave is past the last tile) and stores whole 512-byte half rows.
         l_run += __shfl_xor(l_run, 32, 64);
-        lds_exchange_barrier();  // no DMA is in flight after the last tile
+        wait_vmcnt<0>();         // the empty refills past the last tile have landed
+        lds_exchange_barrier();
         {
             // head and column group from the (opaque) thread index again, not
             // kept live across the tile loop
