@@ -131,34 +131,6 @@ def load_traffic(workload, kernel, path=None):
     return t.get("hbm_bytes_per_launch")
 
 
-def sample_clock(torch, run):
-    """Engine clock (MHz) read from the host through amdsmi while `run()`
-    keeps the GPU busy: median, min and max of the samples, or None where
-    the query is not available."""
-    import threading
-    samples, stop = [], threading.Event()
-
-    def poll():
-        while not stop.is_set():
-            try:
-                samples.append(float(torch.cuda.clock_rate(0)))
-            except Exception:
-                return
-            time.sleep(0.0005)
-
-    t = threading.Thread(target=poll, daemon=True)
-    t.start()
-    run()
-    torch.cuda.synchronize()
-    stop.set()
-    t.join()
-    samples = [x for x in samples if x > 0]
-    if not samples:
-        return None
-    return {"median": statistics.median(samples), "min": min(samples), "max": max(samples),
-            "samples": len(samples), "source": "amdsmi, sampled during 400 back-to-back steps"}
-
-
 def copy_bandwidth(torch, dev, hip, stream, nbytes=1 << 30):
     """Device-to-device copy of 1 GiB (context for the HBM figures): bytes
     read plus bytes written over the best of three copies, GB/s."""
@@ -546,10 +518,12 @@ def main():
     K, W = args.steps, args.warmup
     ev = [[hip.event() for _ in range(4)] for _ in range(K)]
 
-    def step(i=None):
+    def step(i=None, clock=False):
         c = dict(sched)
         if i is not None:
             c["profile_events"] = (ev[i][1].value, ev[i][2].value)
+        if clock:
+            c["record_clock"] = True
         if mtp is not None:
             mla.mla_absorb_q(q_nope, w_uk, q_rope, mtp["q_prime"])
             mla.mla_decode_mtp(mtp["q_prime"].view(w.b, q_len, w.h, D_QK), w.cache, w.seqlens,
@@ -613,7 +587,25 @@ def main():
         hip.record(b1, stream)
         torch.cuda.synchronize()
         b2b_ms = hip.elapsed_ms(b0, b1) / K
-        clock = sample_clock(torch, lambda: [step() for _ in range(400)])
+        # engine clock during the attention kernel, from its first
+        # workgroup's stamps (shader clock against the 100 MHz real-time
+        # counter), over 20 launches after cache eviction
+        ws_t = mtp["ws"] if mtp is not None else bufs.workspace
+        mhz = []
+        for _ in range(20):
+            if flush is not None:
+                flush.sum()
+            ws_t[-mla.CLOCK_BYTES:].zero_()
+            step(clock=True)
+            torch.cuda.synchronize()
+            v = mla.read_clock_mhz(ws_t)
+            if v is not None:
+                mhz.append(v)
+        clock = None if not mhz else {
+            "median": round(statistics.median(mhz), 1), "min": round(min(mhz), 1), "max": round(max(mhz), 1),
+            "launches": len(mhz),
+            "source": "s_memtime / s_memrealtime of the attention kernel's workgroup 0, launches after "
+                      "cache eviction"}
         copy_gbs = copy_bandwidth(torch, dev, hip, stream)
 
     cnt = work_counts(w.b, w.h, lens, elt=w.dtype.itemsize, q_len=q_len)

@@ -30,6 +30,10 @@ MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_HIP = 4
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
+# mla_decode_config_t.reserved[0] bit: record engine-clock stamps in the last
+# CLOCK_BYTES of the workspace (include/mla355.h)
+CONFIG_RECORD_CLOCK = 1
+CLOCK_BYTES = 256
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -186,9 +190,25 @@ def _cfg(config):
         if k == "profile_events":
             c.profile_events[0] = v[0]
             c.profile_events[1] = v[1]
+        elif k == "record_clock":
+            c.reserved[0] = CONFIG_RECORD_CLOCK if v else 0
         else:
             setattr(c, k, int(v))
     return ctypes.pointer(c)
+
+
+def read_clock_mhz(workspace, workspace_bytes=None):
+    """Engine clock (MHz) of the last attention launch made with the config key
+    record_clock: the library's workspace ends with four uint64 stamps (shader
+    clock and 100 MHz real-time counter at the start and the end of the
+    kernel's first workgroup).  workspace_bytes: the size the library reported
+    for the call (default: the whole tensor).  None if nothing was recorded."""
+    n = workspace.numel() if workspace_bytes is None else int(workspace_bytes)
+    st = workspace[n - CLOCK_BYTES:n - CLOCK_BYTES + 32].view(torch.int64).cpu().tolist()
+    c0, r0, c1, r1 = st
+    if r1 <= r0 or c1 <= c0 or r0 == 0:
+        return None
+    return 100.0 * (c1 - c0) / (r1 - r0)
 
 
 def mla_decode_kernel_name(dtype: torch.dtype, h: int, config=None):

@@ -33,10 +33,14 @@ struct Schedule {
 
 int round_down8(int x) { return x < 8 ? 8 : x / 8 * 8; }
 
+static_assert(kClockBytes == MLA_CLOCK_BYTES && kConfigRecordClock == MLA_CONFIG_RECORD_CLOCK,
+              "the clock-stamp hook as the header states it");
+
 mla_status_t choose_schedule(mla_dtype_t dt, int h, const mla_decode_config_t* cfg, Schedule* s)
 {
     if (cfg) {
-        for (int i = 0; i < 5; ++i)
+        if ((cfg->reserved[0] & ~kConfigRecordClock) != 0) return MLA_ERR_UNSUPPORTED;
+        for (int i = 1; i < 5; ++i)
             if (cfg->reserved[i] != 0) return MLA_ERR_UNSUPPORTED;
         if (cfg->n_chunks < 0 || cfg->heads_per_group < 0 || cfg->variant < 0)
             return MLA_ERR_UNSUPPORTED;
@@ -175,6 +179,7 @@ DecodeParams split_params(const void* q_prime, const void* cache, const int32_t*
     p.heads_per_token = rows;
     p.plan_in_kernel = p.plan_min_chunk = 0;
     p.plan_align = 1;
+    p.clock_stamps = (unsigned long long*)(ws + w.clock_off);  // cleared by run_split unless asked for
     p.b = b;
     p.h = rows;
     p.t_max = t_max;
@@ -196,6 +201,7 @@ mla_status_t run_split(DecodeParams p, bool bf16, int min_chunk, int align, bool
 {
     hipEvent_t ev0 = cfg ? (hipEvent_t)cfg->profile_events[0] : nullptr;
     hipEvent_t ev1 = cfg ? (hipEvent_t)cfg->profile_events[1] : nullptr;
+    if (!(cfg && (cfg->reserved[0] & kConfigRecordClock))) p.clock_stamps = nullptr;
     p.plan_in_kernel = kernel_plans && p.b <= kPlanLdsRows && p.n_chunks <= kPlanLdsChunks;
     p.plan_min_chunk = min_chunk;
     p.plan_align = align;
@@ -306,7 +312,8 @@ static hipError_t launch_mtp(const DecodeParams& p, int nw, hipStream_t hs)
 static mla_status_t check_mtp_config(const mla_decode_config_t* cfg)
 {
     if (!cfg) return MLA_OK;
-    for (int i = 0; i < 5; ++i)
+    if ((cfg->reserved[0] & ~kConfigRecordClock) != 0) return MLA_ERR_UNSUPPORTED;
+    for (int i = 1; i < 5; ++i)
         if (cfg->reserved[i] != 0) return MLA_ERR_UNSUPPORTED;
     if (cfg->heads_per_group != 0 || cfg->variant != 0) return MLA_ERR_UNSUPPORTED;
     if (cfg->n_chunks < 0 || cfg->n_chunks % 8 != 0 || cfg->n_chunks > kMaxChunks) return MLA_ERR_UNSUPPORTED;

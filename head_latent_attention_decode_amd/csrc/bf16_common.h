@@ -148,6 +148,20 @@ __device__ __forceinline__ void block_work(int n_chunks, int n_hg, int& k, int& 
     hg = slot % n_hg;
 }
 
+// Opt-in engine-clock stamps (DecodeParams::clock_stamps): the first thread
+// of workgroup 0 records the shader clock and the 100 MHz real-time counter,
+// pair `which` (0: start, 1: end).  A vector store (the thread condition makes
+// the data a per-lane value).
+__device__ __forceinline__ void clock_stamp(unsigned long long* st, int which)
+{
+    if (st != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+        const unsigned long long c = __builtin_amdgcn_s_memtime();
+        const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+        st[2 * which] = c;
+        st[2 * which + 1] = r;
+    }
+}
+
 // Eight OCP e4m3 codes (first in the low byte) -> eight bf16, exact: every
 // e4m3 value is a bf16 value.
 __device__ __forceinline__ bf16x8_t cvt8_e4m3(unsigned long long codes)

@@ -89,7 +89,7 @@ struct Tiling {
 };
 
 template <int WH, int HS, int TS, int NT, int STAGES, bool FP8>
-__global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams p)
+__device__ __forceinline__ void decode_bf16_body(const DecodeParams& p)
 {
     using T = Tiling<WH, HS, TS, NT, STAGES>;
     static_assert(!FP8 || (STAGES == 2 && T::N % T::NW == 0 && T::N <= 64 && WH == 16 && NT == 32 &&
@@ -529,6 +529,14 @@ __global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams 
         ++r;
         while (pv.cu()[r + 1] <= pos) ++r;  // skip empty rows
     }
+}
+
+template <int WH, int HS, int TS, int NT, int STAGES, bool FP8>
+__global__ __launch_bounds__(HS * TS * 64) void decode_bf16_kernel(DecodeParams p)
+{
+    clock_stamp(p.clock_stamps, 0);
+    decode_bf16_body<WH, HS, TS, NT, STAGES, FP8>(p);
+    clock_stamp(p.clock_stamps, 1);
 }
 
 

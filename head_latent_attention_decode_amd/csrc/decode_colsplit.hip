@@ -573,7 +573,9 @@ __device__ __forceinline__ void colsplit_body(const DecodeParams& p)
 template <bool PAGED>
 __global__ __launch_bounds__(256) void decode_colsplit_kernel(DecodeParams p)
 {
+    clock_stamp(p.clock_stamps, 0);
     colsplit_body<PAGED>(p);
+    clock_stamp(p.clock_stamps, 1);
 }
 
 }  // namespace

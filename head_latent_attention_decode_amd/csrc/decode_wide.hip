@@ -502,13 +502,17 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
 template <int NW, int STAGES, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p)
 {
+    clock_stamp(p.clock_stamps, 0);
     decode_wide_body<NW, STAGES, PAGED, false>(p);
+    clock_stamp(p.clock_stamps, 1);
 }
 
 template <int NW, int STAGES, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_wide_causal_kernel(DecodeParams p)
 {
+    clock_stamp(p.clock_stamps, 0);
     decode_wide_body<NW, STAGES, PAGED, true>(p);
+    clock_stamp(p.clock_stamps, 1);
 }
 
 }  // namespace

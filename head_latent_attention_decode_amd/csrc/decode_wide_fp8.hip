@@ -544,7 +544,9 @@ constexpr int kF8Stages = 4;
 
 __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
 {
+    clock_stamp(p.clock_stamps, 0);
     decode_wide_fp8_body<kF8Stages>(p);
+    clock_stamp(p.clock_stamps, 1);
 }
 
 }  // namespace

@@ -48,9 +48,17 @@ struct WorkspaceLayout {
     size_t plan_ints;   // int32 elements of the plan
     size_t plse_off;    // byte offset of partial lse  [slots, h] fp32
     size_t po_off;      // byte offset of partial out  [slots, h, 512] (dtype of the call)
+    size_t clock_off;   // byte offset of the engine-clock stamps (the last kClockBytes)
     size_t total;       // bytes
     int max_slots;
 };
+
+// Engine-clock stamps (opt-in: config reserved[0] bit 0): the attention
+// kernel's workgroup 0 writes four uint64 at clock_off: the shader clock
+// (s_memtime) and the 100 MHz real-time counter (s_memrealtime) at its start,
+// then both again at its end.
+constexpr size_t kClockBytes = 256;
+constexpr int kConfigRecordClock = 1;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -62,7 +70,8 @@ inline WorkspaceLayout workspace_layout(int b, int h, int n_chunks, int part_byt
     w.max_slots = n_chunks + b;  // every chunk adds at most one cut inside a row
     w.plse_off = align_up(w.plan_ints * 4, 256);
     w.po_off = align_up(w.plse_off + (size_t)w.max_slots * h * 4, 256);
-    w.total = align_up(w.po_off + (size_t)w.max_slots * h * kDc * part_bytes, 256);
+    w.clock_off = align_up(w.po_off + (size_t)w.max_slots * h * kDc * part_bytes, 256);
+    w.total = w.clock_off + kClockBytes;
     return w;
 }
 
@@ -97,6 +106,8 @@ struct DecodeParams {
     // plan_align), workgroup 0 leaves a copy at `plan` for the combine, and
     // the attention kernel gives rows with no tokens out = 0, lse = -inf.
     int plan_in_kernel, plan_min_chunk, plan_align;
+    // engine-clock stamps (see kClockBytes), nullptr when not asked for
+    unsigned long long* clock_stamps;
 };
 
 // Largest batch and chunk count whose plan an attention workgroup builds in

@@ -70,11 +70,25 @@ typedef struct {
     int heads_per_group;/* heads one workgroup scores against a shared tile:
                            16, 32, 64 or 128 (bf16), 16 (fp32) */
     int variant;        /* kernel variant index for the chosen head group (0 = auto) */
-    int reserved[5];    /* must be zero */
+    int reserved[5];    /* reserved[0]: MLA_CONFIG_RECORD_CLOCK or 0; the
+                           others must be zero */
     void* profile_events[2]; /* optional hipEvent_t pair, recorded on `stream`
                                 right before and right after the split-KV
                                 attention kernel (both or neither) */
 } mla_decode_config_t;
+
+/* Measurement hook.  With reserved[0] = MLA_CONFIG_RECORD_CLOCK the split-KV
+ * attention kernel's workgroup 0 writes four uint64 into the last
+ * MLA_CLOCK_BYTES of the workspace size the library reports for the call
+ * (mla_*_workspace_bytes*, same arguments and config): the shader clock
+ * (s_memtime) and the 100 MHz real-time counter (s_memrealtime) at its start,
+ * then both again at its end, so the engine clock during the launch is
+ * 100 MHz x (clock difference) / (real-time difference).  The bf16 kernels of
+ * 16 heads per group, the wide-wave, column-split and fp8 kernels write them;
+ * the pair and fp32 kernels write nothing.  Every workspace size includes the
+ * area. */
+#define MLA_CONFIG_RECORD_CLOCK 1
+#define MLA_CLOCK_BYTES 256
 
 int mla_abi_version(void);
 const char* mla_status_string(mla_status_t status);

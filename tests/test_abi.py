@@ -104,13 +104,28 @@ def test_decode_ex_rejects_bad_config(mla):
     lib = ctypes.CDLL(mla.LIB_PATH)
     vp = ctypes.c_void_p
     for cfg in ({"n_chunks": 12}, {"n_chunks": 1 << 20}, {"heads_per_group": 24},
-                {"variant": 9}, {"reserved": (ctypes.c_int * 5)(1, 0, 0, 0, 0)}):
+                {"variant": 9}, {"reserved": (ctypes.c_int * 5)(2, 0, 0, 0, 0)},
+                {"reserved": (ctypes.c_int * 5)(1, 1, 0, 0, 0)}):
         c = mla.MLAConfig()
         for k, v in cfg.items():
             setattr(c, k, v)
         st = lib.mla_decode_ex(1, 2, 16, 100, vp(A), vp(A), vp(A), ctypes.c_float(SCALE), vp(A),
                                vp(A), vp(A), ctypes.c_size_t(1 << 30), ctypes.byref(c), vp(0))
         assert st == 2, cfg
+
+
+def test_record_clock_flag(mla):
+    # reserved[0] = MLA_CONFIG_RECORD_CLOCK is the one accepted non-zero
+    # reserved value; the workspace always ends with the stamp area
+    assert mla.CONFIG_RECORD_CLOCK == 1 and mla.CLOCK_BYTES == 256
+    text = open(os.path.join(ROOT, "include", "mla355.h")).read()
+    assert "#define MLA_CONFIG_RECORD_CLOCK 1" in text and "#define MLA_CLOCK_BYTES 256" in text
+    plain = mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096)
+    assert plain == mla.mla_decode_workspace_bytes(torch.bfloat16, 64, 128, 4096, {"record_clock": True})
+    assert plain % 256 == 0 and plain >= 256
+    assert mla.mla_decode_kernel_name(torch.bfloat16, 128, {"record_clock": True}) == \
+        mla.mla_decode_kernel_name(torch.bfloat16, 128)
+    assert mla.mla_decode_mtp_workspace_bytes(4, 2, 16, 100, {"record_clock": True}) > 0
 
 
 def test_absorb_validation(mla):

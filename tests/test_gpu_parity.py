@@ -590,6 +590,35 @@ def test_full_dsv3_decode_fp8_b64_h128_T4096(mla):
     check_fp8_mfma(out[rows], lse[rows], qd, deq, w.seqlens[rows].tolist(), w.scale, ref_out, ref_lse)
 
 
+# ---------------------------------------------------------------- engine-clock stamps
+
+def test_record_clock_stamps(mla):
+    # the measurement hook: stamps only when asked for, a plausible engine
+    # clock, and the same results either way
+    w = workloads.make_custom(4, 128, [700, 1, 2048, 300], seed=5, device="cuda", poison=False)
+    cases = [({}, "decode_wide_kernel"), ({"heads_per_group": 16}, "decode_bf16_kernel"),
+             ({"heads_per_group": 128, "variant": 6}, "decode_colsplit_kernel")]
+    for cfg, name in cases:
+        assert mla.mla_decode_kernel_name(torch.bfloat16, 128, cfg or None).startswith(name)
+        ws = torch.zeros(mla.mla_decode_workspace_bytes(torch.bfloat16, 4, 128, w.t_max, cfg or None),
+                         dtype=torch.uint8, device="cuda")
+        out, lse = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale, workspace=ws, config=cfg or None)
+        torch.cuda.synchronize()
+        assert mla.read_clock_mhz(ws) is None, name   # not asked for: the area stays zero
+        c = dict(cfg, record_clock=True)
+        out2, lse2 = mla.mla_decode(w.q_prime, w.cache, w.seqlens, w.scale, workspace=ws, config=c)
+        torch.cuda.synchronize()
+        mhz = mla.read_clock_mhz(ws)
+        assert mhz is not None and 300.0 < mhz < 4000.0, (name, mhz)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2), name
+    codes, scale = mla.mla_quantize_cache_fp8(w.cache)
+    ws = torch.zeros(mla.mla_decode_fp8_workspace_bytes(4, 128, w.t_max), dtype=torch.uint8, device="cuda")
+    mla.mla_decode_fp8(w.q_prime, codes, scale, w.seqlens, w.scale, workspace=ws, config={"record_clock": True})
+    torch.cuda.synchronize()
+    mhz = mla.read_clock_mhz(ws)
+    assert mhz is not None and 300.0 < mhz < 4000.0, ("fp8", mhz)
+
+
 # ---------------------------------------------------------------- absorbs, bf16
 
 @pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8)])
