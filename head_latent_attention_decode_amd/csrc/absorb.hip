@@ -17,6 +17,8 @@
 #include "append_layout.h"
 #include "bf16_common.h"
 
+#include <utility>
+
 namespace mla355 {
 namespace {
 
@@ -136,18 +138,23 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
     return c ^ (2 * f);
 }
 
-// Y^T[n, m] = sum_k W[h][k][n] X[m][h][k] for 64 columns n0.. of head h.
+// Y^T[n, m] = sum_k W[h][k][n] X[m][h][k] for 64 NCB columns n0.. of head h.
 //   W  [H][KD][ND] (n contiguous)      X  row m of head h at x + m*x_rs + h*KD
 //   Y  row m of head h at y + m*y_rs + h*y_hs + n
-// Both operands go HBM -> LDS by direct-to-LDS DMA, all of a block's bytes in
-// flight at once (the product is bound by reading the weights): the weight
-// slab W[h][:, n0:n0+64] once, then the head's input rows 64 at a time
-// (16-byte chunk c of staged row m at c ^ (m & 15), so 16 consecutive rows
-// read at one k offset hit 16 distinct bank quads).  4 waves; wave w owns
-// columns n0 + 16w .. +15 (v_mfma_f32_16x16x32_bf16 A rows, read transposed
-// with ds_read_b64_tr_b16); batch rows are the B columns, 16 per block.  When
-// rope != nullptr (q absorb), the workgroups of column block 0 also copy
-// rope[m][h][0:64] to y[...][ND:ND+64].
+// Both operands go HBM -> LDS by direct-to-LDS DMA (the product is bound by
+// reading the weights), in parts of 16 KB: a part is 128 contraction rows of
+// one 64-column weight slab (NCB > 1: slab p, all of KD = 128; NCB = 1: rows
+// 128p .. of the one slab) and, for NCB = 1, the same 128 columns of the
+// head's 64 input rows (NCB > 1: all input columns with part 0).  Every part
+// of row block 0 is requested at once, each into its own LDS object, and each
+// is multiplied as soon as it has landed, while the later parts still stream.
+// Staged input rows are 256 bytes, 16-byte chunk c of row m at c ^ (m & 15),
+// so 16 consecutive rows read at one k offset hit 16 distinct bank quads.
+// 4 waves; wave w owns columns 16w .. +15 of a slab (v_mfma_f32_16x16x32_bf16
+// A rows, read transposed with ds_read_b64_tr_b16); batch rows are the B
+// columns, 16 per block.  Each 64 x 64 output block goes out through LDS as
+// whole 16-byte pieces of its rows.  When rope != nullptr (q absorb), the
+// workgroups of column block 0 also copy rope[m][h][0:64] to y[...][ND:ND+64].
 // blk: this workgroup's index among the product's H * ND / (64 NCB) blocks;
 // OutT: type of Y (bf16, or fp32 for partial sums that are added up later).
 // Block index for workgroup id `id` of `count` when each head has NB blocks
@@ -156,6 +163,18 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
 // the ids 8 NB a + 8 j + x (its block j), and its input rows come from HBM
 // once rather than NB times.  Ids past the last whole group of 8 heads keep
 // their own index.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(IC<I>{}), ...);
+}
+// f(IC<0>{}), ..., f(IC<N - 1>{}): a loop whose index is a compile-time constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int NB>
 __device__ __forceinline__ int xcd_head_block(int id, int count)
 {
@@ -172,75 +191,76 @@ __device__ __forceinline__ void absorb_mfma_body(int blk, int M, int H, const __
                                                  OutT* __restrict__ y, long y_rs, int y_hs,
                                                  const __bf16* __restrict__ rope)
 {
+    static_assert(NCB == 1 ? KD % 128 == 0 : KD == 128, "parts of 128 contraction rows");
     constexpr int NB = ND / (64 * NCB);       // workgroups per head
-    constexpr int KSTEPS = KD / 32;
-    constexpr int W_BYTES = NCB * KD * 128;   // NCB slabs [KD][64]
-    constexpr int X_ROW = KD * 2;             // bytes of one staged input row
-    constexpr int X_BYTES = 64 * X_ROW;       // 64 input rows per block
-    constexpr int W_DMA = W_BYTES / 4096;     // 1 KB DMA instructions per wave
-    constexpr int X_DMA = X_BYTES / 4096;
-    static_assert(W_BYTES % 4096 == 0 && X_BYTES % 4096 == 0, "whole DMA rounds per wave");
+    constexpr int P = NCB > 1 ? NCB : KD / 128;
+    constexpr int KSP = 4;                    // k steps (of 32) per part
+    constexpr int XP = NCB > 1 ? 1 : P;       // staged input parts
+    constexpr int PART = 16384;               // bytes of a weight part, and of an input part
+    constexpr int DMA_W = PART / 4096;        // 1 KB DMA instructions per wave and part
+    constexpr int DMA_X = PART / 4096;
+    constexpr int STG_ROW = 64 * (int)sizeof(OutT) + 16;  // output staging row (padded)
     static_assert(ND % (64 * NCB) == 0, "whole slabs per workgroup");
-    static_assert(X_ROW >= 256, "16 chunks per staged row for the swizzle");
-    lds_byte* slab = stage_lds<W_BYTES, 0>();
-    lds_byte* xs = stage_lds<X_BYTES, 1>();
     const int h = blk / NB;
     const int n0 = (blk % NB) * 64 * NCB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, s = lane & 15;
 
-    // weight slabs (columns n0 + 64cb ..): DMA block j = rows 8(j % (KD/8)) ..
-    // +7 of slab j / (KD/8); lane -> row + lane/8, slot lane%8
-    {
-        const __bf16* wh = w + (size_t)h * KD * ND + n0;
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)wh, (short)0, ((KD - 1) * ND + 64 * NCB) * 2, kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < W_DMA; ++i) {
-            const int j = wave * W_DMA + i;
-            const int cb = j / (KD / 8);
-            const int r = (j % (KD / 8)) * 8 + (lane >> 3);
-            const int c = slab_chunk(r, lane & 7);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(slab + j * 1024), 16,
-                                                     (unsigned)((r * ND + cb * 64 + c * 8) * 2), 0, 0, 0);
-        }
-    }
+    // One LDS object per part (and per staged input part): the compiler then
+    // tracks the DMA of each separately and waits only for the part it reads.
+    auto wpart = [&](auto PI) -> lds_byte* { return stage_lds<PART, 10 + decltype(PI)::value>(); };
+    auto xpart = [&](auto PI) -> lds_byte* { return stage_lds<PART, 20 + decltype(PI)::value>(); };
+    lds_byte* stg = stage_lds<64 * STG_ROW, 30>();
+
+    const __bf16* wh = w + (size_t)h * KD * ND + n0;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)wh, (short)0, ((KD - 1) * ND + 64 * NCB) * 2, kBufferFlags);
     const __bf16* xh = x + (size_t)h * KD;
     const unsigned x_bytes = (unsigned)(((size_t)(M - 1) * x_rs + KD) * 2);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xh, (short)0, x_bytes, kBufferFlags);
-    // input rows mb0*64 .. +63 (rows past M re-read row M-1; never stored)
-    auto stage_x = [&](int mb0) {
+
+    // weight part p: 128 contraction rows (of slab p, or rows 128p.. of the
+    // one slab) x 64 columns; DMA block j = rows 8j .. +7, lane -> row
+    // 8j + lane/8, slot lane%8.
+    auto stage_w = [&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        lds_byte* dst = wpart(PI);
 #pragma unroll
-        for (int i = 0; i < X_DMA; ++i) {
-            const int j = wave * X_DMA + i;
-            const int byte = j * 1024 + lane * 16;
-            const int m = byte / X_ROW;
-            const int c = ((byte % X_ROW) >> 4) ^ (m & 15);
-            const int mg = min(mb0 * 64 + m, M - 1);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (LDS_AS void*)(xs + j * 1024), 16,
-                                                     (unsigned)(((size_t)mg * x_rs + c * 8) * 2), 0, 0, 0);
+        for (int i = 0; i < DMA_W; ++i) {
+            const int j = wave * DMA_W + i;
+            const int r = j * 8 + (lane >> 3);
+            const int c = slab_chunk(r, lane & 7);
+            const int k = NCB > 1 ? r : p * 128 + r;
+            const int cb = NCB > 1 ? p : 0;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(dst + j * 1024), 16,
+                                                     (unsigned)((k * ND + cb * 64 + c * 8) * 2), 0, 0, 0);
         }
     };
-    stage_x(0);
-    if (rope != nullptr && n0 == 0) {
-        for (int i = threadIdx.x; i < M * 8; i += 256) {
-            const int m = i >> 3, c = i & 7;
-            const bf16x8_t v = *(const bf16x8_t*)(rope + ((size_t)m * H + h) * 64 + c * 8);
-            *(bf16x8_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + ND + c * 8) = v;
+    // input part p of row block mb0: rows mb0*64 .. +63 (rows past M re-read
+    // row M-1; never stored), contraction columns 128p .. +127 as 256-byte rows,
+    // 16-byte chunk c of row m at c ^ (m & 15).
+    auto stage_x = [&](auto PI, int mb0) {
+        constexpr int p = decltype(PI)::value;
+        lds_byte* dst = xpart(PI);
+#pragma unroll
+        for (int i = 0; i < DMA_X; ++i) {
+            const int j = wave * DMA_X + i;
+            const int m = j * 4 + (lane >> 4);
+            const int c = (lane & 15) ^ (m & 15);
+            const int mg = min(mb0 * 64 + m, M - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (LDS_AS void*)(dst + j * 1024), 16,
+                                                     (unsigned)(((size_t)mg * x_rs + p * 128 + c * 8) * 2), 0, 0, 0);
         }
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
+    };
 
-    // A operand (W^T rows n, k-slots g*8 .. +7) for every k step of a slab.
+    // A operand (W^T rows n, k-slots g*8 .. +7) for the 4 k steps of a part.
     // tr16 mapping: source lane s of a 16-lane group supplies row k0 + g*8 + s/4
     // (+4 for the upper half), columns 4*(s%4) .. +3 of the wave's 16 columns.
-    const int g = lane >> 4, s = lane & 15;
     const int col = wave * 16 + 4 * (s & 3);
-    auto read_a = [&](int cb, bf16x8_t (&a)[KSTEPS]) {
-        const lds_byte* sl = slab + cb * KD * 128;
+    auto read_a = [&](const lds_byte* sl, bf16x8_t (&a)[KSP]) {
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
+        for (int ks = 0; ks < KSP; ++ks) {
             const int r0 = ks * 32 + g * 8 + (s >> 2);
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (LDS_AS i16x4_t*)(sl + r0 * 128 + (slab_chunk(r0, col >> 3) << 4) + (col & 7) * 2));
@@ -250,46 +270,128 @@ __device__ __forceinline__ void absorb_mfma_body(int blk, int M, int H, const __
                                             0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    bf16x8_t a[KSTEPS];
-    if (NCB == 1) read_a(0, a);
-
-    for (int mb0 = 0; mb0 * 64 < M; ++mb0) {
-        if (mb0 > 0) {
-            __syncthreads();  // every wave is done with the previous block
-            stage_x(mb0);
-            wait_vmcnt<0>();
-            __syncthreads();
-        }
+    // acc[mb] += W-part^T . X-part^T for batch rows mb*16 + s (B operand:
+    // staged row mb*16 + s, k-slots g*8 .. +7 of each step).
+    auto mma_part = [&](const lds_byte* wl, const lds_byte* xl, f32x4_t (&acc)[4]) {
+        bf16x8_t a[KSP];
+        read_a(wl, a);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            if (NCB > 1) read_a(cb, a);
+        for (int mb = 0; mb < 4; ++mb) {
+            const lds_byte* xr = xl + (mb * 16 + s) * 256;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                // B operand: staged row mb*16 + s, k-slots g*8 .. +7 of step ks
-                const lds_byte* xr = xs + (mb * 16 + s) * X_ROW;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const bf16x8_t b = *(const LDS_AS bf16x8_t*)(xr + (((ks * 4 + g) ^ s) << 4));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc, 0, 0, 0);
-                }
-                // acc[i]: output column n0 + 64cb + 16*wave + g*4 + i of batch row m
-                const int m = mb0 * 64 + mb * 16 + s;
-                if (m < M) {
-                    OutT* dst = y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + cb * 64 + wave * 16 + g * 4;
-                    if constexpr (sizeof(OutT) == 2) {
-                        bf16x4_t o;
-                        o[0] = (__bf16)acc[0];
-                        o[1] = (__bf16)acc[1];
-                        o[2] = (__bf16)acc[2];
-                        o[3] = (__bf16)acc[3];
-                        *(bf16x4_t*)dst = o;
-                    } else {
-                        *(f32x4_t*)dst = acc;
-                    }
-                }
+            for (int ks = 0; ks < KSP; ++ks) {
+                const bf16x8_t b = *(const LDS_AS bf16x8_t*)(xr + (((ks * 4 + g) ^ s) << 4));
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc[mb], 0, 0, 0);
             }
         }
+    };
+    // Output block (64 batch rows x 64 columns n0 + 64cb ..) through LDS, so
+    // that each row goes out as whole 16-byte pieces of one 128-byte (bf16) or
+    // 256-byte (fp32) run.  acc[mb][i]: row mb*16 + s, column 16 wave + 4g + i.
+    auto store_block = [&](const f32x4_t (&acc)[4], int mb0, int cb) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            lds_byte* d = stg + (mb * 16 + s) * STG_ROW + (wave * 16 + g * 4) * (int)sizeof(OutT);
+            if constexpr (sizeof(OutT) == 2) {
+                bf16x4_t o;
+                o[0] = (__bf16)acc[mb][0];
+                o[1] = (__bf16)acc[mb][1];
+                o[2] = (__bf16)acc[mb][2];
+                o[3] = (__bf16)acc[mb][3];
+                *(LDS_AS bf16x4_t*)d = o;
+            } else {
+                *(LDS_AS f32x4_t*)d = acc[mb];
+            }
+        }
+        lds_exchange_barrier();
+        constexpr int PIECES = 64 * (int)sizeof(OutT) / 16;  // 16-byte pieces per row
+        constexpr int ROWS_PER_PASS = 256 / PIECES;
+#pragma unroll
+        for (int r0 = 0; r0 < 64; r0 += ROWS_PER_PASS) {
+            const int rr = r0 + threadIdx.x / PIECES, pc = threadIdx.x % PIECES;
+            const int m = mb0 * 64 + rr;
+            const bf16x8_t v = *(const LDS_AS bf16x8_t*)(stg + rr * STG_ROW + pc * 16);
+            if (m < M)
+                *(bf16x8_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + n0 + cb * 64 +
+                             pc * (16 / (int)sizeof(OutT))) = v;
+        }
+        lds_exchange_barrier();  // staging free for the next block
+    };
+    // q absorb: rope[m][h][0:64] -> y[...][ND:ND+64] for the rows of block mb0
+    // (workgroups of column block 0; two 16-byte pieces per thread).  Loaded
+    // before the DMAs (rows past M re-read row M-1, unconditionally: a
+    // per-lane branch around the load makes the compiler wait for it at once)
+    // and stored at the end of the block.
+    bf16x8_t rv[2];
+    auto rope_load = [&](int mb0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = threadIdx.x + 256 * u;
+            const int m = min(mb0 * 64 + (i >> 3), M - 1), c = i & 7;
+            rv[u] = *(const bf16x8_t*)(rope + ((size_t)m * H + h) * 64 + c * 8);
+        }
+    };
+    auto rope_store = [&](int mb0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = threadIdx.x + 256 * u;
+            const int m = mb0 * 64 + (i >> 3), c = i & 7;
+            if (m < M) *(bf16x8_t*)(y + (size_t)m * y_rs + (size_t)h * y_hs + ND + c * 8) = rv[u];
+        }
+    };
+    const bool do_rope = rope != nullptr && n0 == 0;
+
+    // ---- row block 0: every part in flight at once, each consumed as it lands
+    auto zero = [](f32x4_t (&acc)[4]) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    };
+
+    // ---- row block 0: every part in flight at once, each consumed as it lands
+    if (do_rope) rope_load(0);
+    static_for<P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        if constexpr (NCB == 1 || p == 0) stage_x(PI, 0);
+        stage_w(PI);
+    });
+    {
+        f32x4_t acc[4];
+        zero(acc);
+        static_for<P>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            // this wave's DMAs of the later parts may stay in flight; the
+            // barrier then makes part p of every wave visible
+            wait_vmcnt<(P - 1 - p) * (DMA_W + (NCB == 1 ? DMA_X : 0))>();
+            lds_exchange_barrier();
+            mma_part(wpart(PI), xpart(IC<NCB == 1 ? p : 0>{}), acc);
+            if constexpr (NCB > 1) {
+                store_block(acc, 0, p);
+                zero(acc);
+            }
+        });
+        if constexpr (NCB == 1) store_block(acc, 0, 0);
+    }
+    if (do_rope) rope_store(0);
+
+    // ---- further row blocks (more than 64 batch rows): restage the input
+    for (int mb0 = 1; mb0 * 64 < M; ++mb0) {
+        if (do_rope) rope_load(mb0);
+        lds_exchange_barrier();  // every wave is done with the previous block's input
+        static_for<XP>([&](auto PI) { stage_x(PI, mb0); });
+        wait_vmcnt<0>();
+        lds_exchange_barrier();
+        f32x4_t acc[4];
+        zero(acc);
+        static_for<P>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            mma_part(wpart(PI), xpart(IC<NCB == 1 ? p : 0>{}), acc);
+            if constexpr (NCB > 1) {
+                store_block(acc, mb0, p);
+                zero(acc);
+            }
+        });
+        if constexpr (NCB == 1) store_block(acc, mb0, 0);
+        if (do_rope) rope_store(mb0);
     }
 }
 
