@@ -8,12 +8,13 @@
 //             the 512-wide attention output.
 // Both are per-head products with a 128 x 512 weight block used by only b
 // query rows, so they are weight-read bound at small b.  bf16: one workgroup
-// per (head, 64 output columns) DMAs that weight slab and the head's input
-// rows (64 at a time) into LDS with every byte in flight at once, reads the
-// slab transposed (ds_read_b64_tr_b16) as the A operand of
-// v_mfma_f32_16x16x32_bf16 and the input rows as the B operand, fp32
-// accumulation.  fp32: the vector-ALU kernels below (IEEE fp32 FMAs), one
-// workgroup per (head, block of 16 batch rows).
+// per (head, 64 or 256 output columns) DMAs its weight slabs and the head's
+// input rows (64 at a time) into LDS in 16 KB parts, all requested at once
+// and each multiplied as it lands, reads the slab transposed
+// (ds_read_b64_tr_b16) as the A operand of v_mfma_f32_16x16x32_bf16 and the
+// input rows as the B operand, fp32 accumulation.  fp32: the vector-ALU
+// kernels below (IEEE fp32 FMAs), one workgroup per (head, block of 16 batch
+// rows).
 #include "append_layout.h"
 #include "bf16_common.h"
 
@@ -138,6 +139,34 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
     return c ^ (2 * f);
 }
 
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(IC<I>{}), ...);
+}
+// f(IC<0>{}), ..., f(IC<N - 1>{}): a loop whose index is a compile-time constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Block index for workgroup id `id` of `count` when each head has NB blocks
+// that read the same input rows.  Workgroups go to the 8 XCDs round-robin by
+// id, so ids that are equal mod 8 share one XCD and its L2: head 8a + x gets
+// the ids 8 NB a + 8 j + x (its block j), and its input rows come from HBM
+// once rather than NB times.  Ids past the last whole group of 8 heads keep
+// their own index.
+template <int NB>
+__device__ __forceinline__ int xcd_head_block(int id, int count)
+{
+    constexpr int kSpan = 8 * NB;
+    const int full = count / kSpan * kSpan;
+    if (id >= full) return id;
+    const int a = id / kSpan, rem = id % kSpan;
+    return (8 * a + rem % 8) * NB + rem / 8;
+}
+
 // Y^T[n, m] = sum_k W[h][k][n] X[m][h][k] for 64 NCB columns n0.. of head h.
 //   W  [H][KD][ND] (n contiguous)      X  row m of head h at x + m*x_rs + h*KD
 //   Y  row m of head h at y + m*y_rs + h*y_hs + n
@@ -157,34 +186,6 @@ __device__ __forceinline__ int slab_chunk(int r, int c)
 // workgroups of column block 0 also copy rope[m][h][0:64] to y[...][ND:ND+64].
 // blk: this workgroup's index among the product's H * ND / (64 NCB) blocks;
 // OutT: type of Y (bf16, or fp32 for partial sums that are added up later).
-// Block index for workgroup id `id` of `count` when each head has NB blocks
-// that read the same input rows.  Workgroups go to the 8 XCDs round-robin by
-// id, so ids that are equal mod 8 share one XCD and its L2: head 8a + x gets
-// the ids 8 NB a + 8 j + x (its block j), and its input rows come from HBM
-// once rather than NB times.  Ids past the last whole group of 8 heads keep
-// their own index.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>)
-{
-    (f(IC<I>{}), ...);
-}
-// f(IC<0>{}), ..., f(IC<N - 1>{}): a loop whose index is a compile-time constant.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-template <int NB>
-__device__ __forceinline__ int xcd_head_block(int id, int count)
-{
-    constexpr int kSpan = 8 * NB;
-    const int full = count / kSpan * kSpan;
-    if (id >= full) return id;
-    const int a = id / kSpan, rem = id % kSpan;
-    return (8 * a + rem % 8) * NB + rem / 8;
-}
-
 template <int KD, int ND, int NCB, typename OutT>
 __device__ __forceinline__ void absorb_mfma_body(int blk, int M, int H, const __bf16* __restrict__ x,
                                                  long x_rs, const __bf16* __restrict__ w,
