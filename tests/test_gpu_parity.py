@@ -857,6 +857,24 @@ def test_cache_append_every_row(mla, d_model):
     assert sl.cpu().tolist() == lens
 
 
+def test_cache_append_more_than_64_rows(mla):
+    # 100 rows: the projection's second block of 64 input rows (ragged: 36),
+    # with its fp32 partial sums staged and stored as 256-byte row pieces
+    rng = np.random.default_rng(97)
+    b, t_max, n_pos, d_model = 100, 24, 24, 768
+    lens = [int(v) for v in rng.integers(-2, t_max + 2, size=b)]
+    x, wd, wr, cos_t, sin_t, cache = _append_inputs(b, d_model, t_max, n_pos, seed=97)
+    before = cache.clone()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sl_out = torch.empty_like(sl)
+    mla.mla_cache_append(x, wd, wr, cos_t, sin_t, cache, sl, sl_out)
+    torch.cuda.synchronize()
+    ref = oracle.cache_append(x.cpu(), wd.cpu(), wr.cpu(), cos_t.cpu(), sin_t.cpu(), np.array(lens, np.int32),
+                              before.cpu())
+    _check_append(before, cache, ref, lens, t_max, n_pos)
+    assert sl_out.cpu().tolist() == [L + 1 if 0 <= L < t_max else L for L in lens]
+
+
 def test_cache_append_in_place_lengths_and_table_bound(mla):
     # seqlens updated in place; a position past the tables (n_pos < t_max) is not written
     lens = [3, 10, 9]
