@@ -621,9 +621,10 @@ def test_record_clock_stamps(mla):
 
 # ---------------------------------------------------------------- absorbs, bf16
 
-@pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8)])
+@pytest.mark.parametrize("b,h", [(64, 128), (100, 16), (3, 8), (70, 13)])
 def test_absorbs_bf16(mla, b, h):
-    # b = 100: two rounds of the 64-row load groups, the second one ragged
+    # b = 100: two rounds of the 64-row load groups, the second one ragged;
+    # h = 13: workgroups past the last whole group of 8 heads keep their ids
     q_nope, q_rope, w_uk, w_uv = workloads.make_step_weights(b, h, device="cuda")
     qp = mla.mla_absorb_q(q_nope, w_uk, q_rope)
     o = torch.randn(b, h, 512, device="cuda").to(torch.bfloat16)
