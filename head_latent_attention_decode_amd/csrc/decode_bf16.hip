@@ -38,6 +38,7 @@
 #include "variants.h"
 
 #include <array>
+#include <type_traits>
 #include <utility>
 
 #include <math.h>
@@ -100,6 +101,14 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeParams& p)
                   "fp8 merge area");
     using M = Mfma<WH>;
     typedef typename M::acc_t acc_t;
+    // An operand fragment as read from LDS: 8 bf16, or (fp8) 8 e4m3 codes.
+    typedef std::conditional_t<FP8, unsigned long long, bf16x8_t> kraw_t;
+    auto to_bf16x8 = [](kraw_t f) -> bf16x8_t {
+        if constexpr (FP8)
+            return cvt8_e4m3(f);
+        else
+            return f;
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -335,21 +344,27 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeParams& p)
                 if (ks < T::KSTEPS_A) return tb + koffA[ks % NQA] + (ks / NQA) * 256 + sb * WH * 1024;
                 return tb + koffB[ks - T::KSTEPS_A] + sb * WH * 128;
             };
-            auto k_frag = [&](int idx) -> bf16x8_t {
-                if (!FP8) return *(const LDS_AS bf16x8_t*)k_addr(idx);
-                const int ks = idx / T::SBLK, sb = idx % T::SBLK;
-                return cvt8_e4m3(*(const LDS_AS unsigned long long*)(sg + k8off[sb] + k8x[sb][ks & 1] + 64 * (ks >> 1)));
+            // The ring holds fragments as read (fp8: raw codes); an fp8
+            // fragment is converted only where its MFMA takes it, so the
+            // conversion does not wait for a read issued in the same step.
+            auto k_frag = [&](int idx) -> kraw_t {
+                if constexpr (!FP8) {
+                    return *(const LDS_AS bf16x8_t*)k_addr(idx);
+                } else {
+                    const int ks = idx / T::SBLK, sb = idx % T::SBLK;
+                    return *(const LDS_AS unsigned long long*)(sg + k8off[sb] + k8x[sb][ks & 1] + 64 * (ks >> 1));
+                }
             };
             acc_t sacc[T::SBLK][2];
 #pragma unroll
             for (int sb = 0; sb < T::SBLK; ++sb) sacc[sb][0] = sacc[sb][1] = (acc_t){};
-            bf16x8_t kring[PF];
+            kraw_t kring[PF];
 #pragma unroll
             for (int i = 0; i < PF; ++i) kring[i] = k_frag(i);
 #pragma unroll
             for (int idx = 0; idx < NSTEP; ++idx) {
                 const int ks = idx / T::SBLK, sb = idx % T::SBLK;
-                const bf16x8_t kf = kring[idx % PF];
+                const bf16x8_t kf = to_bf16x8(kring[idx % PF]);
                 if (idx + PF < NSTEP) kring[idx % PF] = k_frag(idx + PF);
                 sacc[sb][ks & 1] = M::mma(kf, qf[ks], sacc[sb][ks & 1]);
                 __builtin_amdgcn_sched_barrier(0);
@@ -419,30 +434,31 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeParams& p)
             constexpr int TPU = (WH == 16) ? 32 : 16;
             constexpr int NPV = NPB * T::MBLK;
             constexpr int PFV = 4;
-            auto v_frag = [&](int idx) -> bf16x8_t {
+            auto v_frag = [&](int idx) -> kraw_t {
                 const int u = idx / T::MBLK, mb = idx % T::MBLK;
-                if (FP8) {
+                if constexpr (FP8) {
                     typedef int v2i_t __attribute__((ext_vector_type(2)));
                     const v2i_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (LDS_AS v2i_t*)(sg + v8off + v8x[mb & 3] + 64 * (mb >> 2)));
-                    return cvt8_e4m3(__builtin_bit_cast(unsigned long long, c));
+                    return __builtin_bit_cast(unsigned long long, c);
+                } else {
+                    const int q = mb % NQV;
+                    const int blk = (mb / NQV) * 256 + u * TPU * 1024;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4_t*)(tb + voff0[q] + blk));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4_t*)(tb + (WH == 16 ? voff0[q] + 16 * 1024 : voff1[q]) + blk));
+                    return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                                   __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
                 }
-                const int q = mb % NQV;
-                const int blk = (mb / NQV) * 256 + u * TPU * 1024;
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS i16x4_t*)(tb + voff0[q] + blk));
-                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS i16x4_t*)(tb + (WH == 16 ? voff0[q] + 16 * 1024 : voff1[q]) + blk));
-                return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                               __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
             };
-            bf16x8_t vring[PFV];
+            kraw_t vring[PFV];
 #pragma unroll
             for (int i = 0; i < PFV; ++i) vring[i] = v_frag(i);
 #pragma unroll
             for (int idx = 0; idx < NPV; ++idx) {
                 const int u = idx / T::MBLK, mb = idx % T::MBLK;
-                const bf16x8_t a = vring[idx % PFV];
+                const bf16x8_t a = to_bf16x8(vring[idx % PFV]);
                 if (idx + PFV < NPV) vring[idx % PFV] = v_frag(idx + PFV);
                 o[mb] = M::mma(a, pb[u], o[mb]);
                 __builtin_amdgcn_sched_barrier(0);
