@@ -111,7 +111,8 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeParams& p)
     };
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index is uniform: keep it (and the DMA row arithmetic built on it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hs = wave % HS;
     const int ts = wave / HS;
     const int hl = lane & (WH - 1);   // this lane's head inside the wave's WH heads
