@@ -60,9 +60,9 @@ struct WideF8Tiling {
     static constexpr int SCL_OFF = B_OFF + N * 64;   // the tile's 32 token scales (64 slots)
     static constexpr int TILE_BYTES = SCL_OFF + 64 * 4;
     static constexpr int LOADS_A = 16 / NW;          // two rows per DMA instruction
-    // plus one instruction per wave: region B (waves 0, 1: 16 rows each) or
-    // the 32 scales (waves 2 and 3, the same bytes)
-    static constexpr int LOADS = LOADS_A + 1;
+    // plus two instructions per wave: a region-B block of 16 rows (waves w
+    // and w + 2 the same rows) and the 32 scales (every wave the same bytes)
+    static constexpr int LOADS = LOADS_A + 2;
     static constexpr int KS = kDqk / 64;             // 9 score steps of 64 channels
     static constexpr int MBLK = kDc / 32;            // 16 output blocks of 32 columns
     static constexpr int STG_ROW = 512 + 16;         // epilogue staging row (bf16 half rows)
@@ -258,18 +258,24 @@ __device__ __forceinline__ void decode_wide_fp8_body(const DecodeParams& p)
                 const int c = (ln & 31) ^ sw8(row);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + q * 1024), 16,
                                                          (unsigned)(srow * T::ROW8 + c * 16), 0, 0, 0);
-            } else if (wave < 2) {
-                // region B rows 16 wave .. +15: lane -> row 16 wave + l / 4, position l % 4
-                const int row = 16 * wave + (ln >> 2);
+            } else if (li == T::LOADS_A) {
+                // region B rows 16 bw .. +15, bw = wave & 1: lane -> row
+                // 16 bw + l / 4, position l % 4 (waves 2 and 3 write the same
+                // bytes as waves 0 and 1)
+                const int bw = wave & 1;
+                const int row = 16 * bw + (ln >> 2);
                 const int srow = min(row, last);
                 const int c = (ln & 3) ^ ((row >> 2) & 3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::B_OFF + wave * 1024), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(st + T::B_OFF + bw * 1024), 16,
                                                          (unsigned)(srow * T::ROW8 + 512 + c * 16), 0, 0, 0);
             } else {
                 // the tile's scales, 4 bytes per lane (dword bounds checks:
                 // tokens past the segment end read 0; lanes 32..63 fill the
-                // unused rest of the scale area).  Waves 2 and 3 write the
-                // same bytes.
+                // unused rest of the scale area); every wave writes the same
+                // bytes.  Every wave thus issues the same instruction kinds
+                // in the same order: with a wave-dependent choice between the
+                // region-B and the scale DMA here, the compiler drained the
+                // whole ring before the first stage's scale reads.
                 const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(seg_scale + t0), (short)0, (last + 1) * 4, kBufferFlags);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (LDS_AS void*)(st + T::SCL_OFF), 4,
