@@ -182,6 +182,29 @@ __device__ __forceinline__ bf16x8_t cvt8_e4m3(unsigned long long codes)
     return (bf16x8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
+// 32x32x16 score MFMAs with the accumulator in VGPRs, for kernels whose
+// output sums take all 256 AGPRs: given the builtin, the compiler picks one
+// register form for every MFMA of a kernel, places the score accumulator in
+// AGPRs as well and parks an output block in VGPRs around every score chain.
+// The hazard recognizer does not look inside asm: score_wait() supplies the
+// wait states between the last MFMA of a chain and the first vector-ALU
+// access to its result (more than the 12 that a dependent read of an 8-pass
+// result needs).
+__device__ __forceinline__ f32x16_t score_first(bf16x8_t a, bf16x8_t b)
+{
+    f32x16_t d;
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ void score_acc(f32x16_t& acc, bf16x8_t a, bf16x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_wait(f32x16_t& acc)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
 // Region-B swizzle (3 bits, 128-byte rows): rows of equal parity distinct.
 __device__ __forceinline__ int xb(int r) { return (r >> 1) & 7; }
 

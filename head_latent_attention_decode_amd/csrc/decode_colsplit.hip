@@ -89,27 +89,6 @@ struct ColTiling {
 
 typedef const __attribute__((address_space(4))) int32_t cint32c_t;
 
-// Score MFMAs with the accumulator in VGPRs: the 256 AGPRs hold the output
-// accumulators, and the compiler picks one register form for every MFMA of a
-// kernel, so these are written as inline asm.  The hazard recognizer does not
-// look inside asm: score_wait() supplies the wait states between the last
-// score MFMA and the first vector-ALU access to its result (more than the 12
-// a dependent read of an 8-pass result needs).
-__device__ __forceinline__ f32x16_t score_first(bf16x8_t a, bf16x8_t b)
-{
-    f32x16_t d;
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-    return d;
-}
-__device__ __forceinline__ void score_acc(f32x16_t& acc, bf16x8_t a, bf16x8_t b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void score_wait(f32x16_t& acc)
-{
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
-}
-
 template <bool PAGED>
 __device__ __forceinline__ void colsplit_body(const DecodeParams& p)
 {

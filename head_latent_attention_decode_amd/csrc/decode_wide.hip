@@ -346,10 +346,14 @@ __device__ __forceinline__ void decode_wide_body(const DecodeParams& p)
                 for (int j = 0; j < T::KS; ++j) {
                     const bf16x8_t kf = kring[j % PF];
                     if (j + PF < T::KS) kring[j % PF] = k_frag(tb, j + PF);
-                    sacc = (j == 0) ? M::mma(kf, qf[j], (acc_t){}) : M::mma(kf, qf[j], sacc);
+                    if (j == 0)
+                        sacc = score_first(kf, qf[j]);
+                    else
+                        score_acc(sacc, kf, qf[j]);
                     if (j < T::LOADS) issue_load(IC<SR>{}, rptr, i + STAGES - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                score_wait(sacc);
             }
 
             // ---- online softmax; sacc[e]: token (e/4)*8 + 4grp + e%4, head hl
